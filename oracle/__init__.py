@@ -1,0 +1,29 @@
+"""fp64 CPU oracle for the single-pass fused cascaded-reduction attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import it.
+The library under ``attention_pass_cascaded_amd`` never imports, links or
+calls anything here, and this package imports nothing from there: the two
+share no code.  Inputs come from ``workloads`` (random draws only).
+
+Contents
+  cascade.py    the unfused three-pass cascade (max pass, exp-sum pass,
+                P.V pass), the incremental (m, l, O) form, split-KV partials
+                and the log-sum-exp merge, RoPE.  numpy, float64.
+  brute.py      pure-Python scalar reference for tiny inputs (math.exp,
+                math.fsum), written from the textbook softmax definition.
+
+Every function is pinned by ``tests/test_oracle.py`` (brute force, closed
+forms, invariants and a library routine the definition reduces to).
+"""
+from .cascade import (  # noqa: F401
+    attention,
+    attention_incremental,
+    attention_rows,
+    lse_merge,
+    query_positions,
+    rope_rotate,
+    split_partials,
+    visible_mask,
+    softmax_probs,
+)

@@ -1,0 +1,285 @@
+"""Pins for the fp64 oracle, against things other than itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped max
+shift, a wrong sign or index in RoPE, a transposed operand, an off-by-one in
+the window, a wrong GQA head map, a wrong merge weight) fails at least one test:
+  * pure-Python brute force with the textbook (unshifted) softmax;
+  * hand-worked cases in tests/golden/hand_cases.json;
+  * closed forms (one key, zero scores, constant V, W=1, W >= Nk);
+  * invariants (rows of P sum to 1, incremental == three-pass for any tiling
+    and tile order, split+merge == unsplit, tree merge == flat merge, shift
+    invariance of safe softmax, RoPE relative-position property);
+  * a library routine the definition reduces to without RoPE (torch's
+    scaled_dot_product_attention in float64 on the CPU, and logsumexp).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cascade as A
+from oracle.brute import brute_attention
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def close(a, b, rtol=1e-12, atol=1e-12):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), "different infinities"
+    assert np.array_equal(a[~fin], b[~fin])
+    np.testing.assert_allclose(a[fin], b[fin], rtol=rtol, atol=atol)
+
+
+CASES = [
+    # (B, Hq, Hkv, Nq, Nk, D, mask, window, rope_base)
+    (1, 1, 1, 6, 6, 4, "none", 0, 0.0),
+    (2, 2, 2, 5, 5, 8, "causal", 0, 0.0),
+    (1, 4, 2, 7, 9, 4, "causal", 0, 0.0),      # Nq < Nk, GQA 4:2
+    (1, 2, 1, 9, 6, 4, "causal", 0, 0.0),      # Nq > Nk: leading rows see nothing
+    (1, 2, 2, 8, 8, 4, "sliding", 1, 0.0),
+    (2, 1, 1, 9, 9, 6, "sliding", 3, 0.0),
+    (1, 4, 2, 5, 11, 4, "sliding", 4, 0.0),
+    (1, 1, 1, 6, 6, 8, "none", 0, 10000.0),
+    (1, 2, 2, 7, 7, 4, "causal", 0, 10000.0),
+    (1, 4, 2, 6, 10, 8, "causal", 0, 100.0),
+    (1, 2, 1, 9, 9, 4, "sliding", 3, 500.0),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,D,mask,window,base", CASES)
+def test_three_pass_matches_brute_force(B, Hq, Hkv, Nq, Nk, D, mask, window, base):
+    seed = hash((B, Hq, Hkv, Nq, Nk, D, mask, window, base)) % 2**31
+    q, k, v = rnd((B, Hq, Nq, D), seed), rnd((B, Hkv, Nk, D), seed + 1), rnd((B, Hkv, Nk, D), seed + 2)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.attention(q, k, v, scale, mask, window, base)
+    ob, lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), scale, mask, window, base)
+    close(o, ob)
+    close(lse, lb)
+    # the same rows one at a time
+    rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(Nq)]
+    orow, lrow = oracle.attention_rows(q, k, v, scale, rows, mask, window, base)
+    close(orow, o.reshape(-1, D))
+    close(lrow, lse.reshape(-1))
+
+
+def test_hand_cases():
+    g = json.load(open(GOLD))
+    for c in g["attention"]:
+        o, lse = oracle.attention(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]),
+                                  c["scale"], c["mask"], c["window"], c["rope_base"])
+        close(o, c["o"], rtol=1e-14, atol=1e-14)
+        close(lse, c["lse"], rtol=1e-14, atol=1e-14)
+    for c in g["rope"]:
+        out = oracle.rope_rotate(np.array([c["x"]]), np.array([c["pos"]]), c["base"])
+        close(out[0], c["out"], rtol=1e-14, atol=1e-15)
+    for c in g["merge"]:
+        lp = np.array([float(x) for x in c["lse_parts"]])
+        o, lse = oracle.lse_merge(np.array(c["o_parts"]), lp)
+        close(o, c["o"], rtol=1e-14, atol=1e-15)
+        close(lse, c["lse"], rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("mask,window,base", [("none", 0, 0.0), ("causal", 0, 0.0),
+                                              ("sliding", 5, 0.0), ("causal", 0, 10000.0)])
+def test_rows_of_p_sum_to_one(mask, window, base):
+    q, k = rnd((1, 2, 33, 8), 3), rnd((1, 2, 40, 8), 4)
+    for h in range(2):
+        P = oracle.softmax_probs(q, k, 0.3, mask, window, base, b=0, h=h)
+        vis = A.visible_mask(A.query_positions(33, 40), np.arange(40), mask, window)
+        assert np.all(P[~vis] == 0.0)
+        np.testing.assert_allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask,window,base", [("none", 0, 0.0), ("causal", 0, 0.0),
+                                              ("sliding", 7, 0.0), ("causal", 0, 10000.0),
+                                              ("sliding", 20, 10000.0)])
+@pytest.mark.parametrize("tile", [1, 3, 64, 128, 150])
+def test_incremental_equals_three_pass(mask, window, base, tile):
+    q, k, v = rnd((1, 2, 150, 8), 10), rnd((1, 1, 150, 8), 11), rnd((1, 1, 150, 8), 12)
+    o, lse = oracle.attention(q, k, v, 0.35, mask, window, base)
+    oi, li = oracle.attention_incremental(q, k, v, 0.35, mask, window, base, tile=tile)
+    close(oi, o)
+    close(li, lse)
+
+
+def test_incremental_is_order_independent():
+    q, k, v = rnd((1, 1, 70, 8), 20), rnd((1, 1, 130, 8), 21), rnd((1, 1, 130, 8), 22)
+    o, lse = oracle.attention(q, k, v, 0.5, "causal")
+    ntiles = -(-130 // 16)
+    for seed in range(3):
+        order = np.random.default_rng(seed).permutation(ntiles)
+        oi, li = oracle.attention_incremental(q, k, v, 0.5, "causal", tile=16, order=order)
+        close(oi, o)
+        close(li, lse)
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 64])
+@pytest.mark.parametrize("mask,window,base", [("none", 0, 0.0), ("causal", 0, 0.0),
+                                              ("sliding", 9, 10000.0)])
+def test_split_merge_equals_unsplit(S, mask, window, base):
+    q, k, v = rnd((2, 4, 3, 8), 30), rnd((2, 2, 100, 8), 31), rnd((2, 2, 100, 8), 32)
+    o, lse = oracle.attention(q, k, v, 0.4, mask, window, base)
+    op, lp = oracle.split_partials(q, k, v, 0.4, S, mask, window, base)
+    om, lm = oracle.lse_merge(op, lp)
+    close(om, o)
+    close(lm, lse)
+
+
+def test_tree_merge_equals_flat_merge():
+    op, lp = rnd((5, 16, 6), 40), rnd((5, 16), 41, 3.0)
+    lp[1, 3] = -np.inf
+    of, lf = oracle.lse_merge(op, lp)
+    oa, la = oracle.lse_merge(op[:, :5], lp[:, :5])
+    ob, lb = oracle.lse_merge(op[:, 5:11], lp[:, 5:11])
+    oc, lc = oracle.lse_merge(op[:, 11:], lp[:, 11:])
+    ot, lt = oracle.lse_merge(np.stack([oa, ob, oc], axis=1), np.stack([la, lb, lc], axis=1))
+    close(ot, of)
+    close(lt, lf)
+
+
+def test_split_bounds_cover_keys_once():
+    for Nk, S in [(32768, 64), (100, 7), (5, 8), (1, 1)]:
+        b = A.split_bounds(Nk, S)
+        covered = [j for lo, hi in b for j in range(lo, hi)]
+        assert covered == list(range(Nk))
+        if Nk == 32768:
+            assert all(hi - lo == 512 for lo, hi in b)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_single_key():
+    q, k, v = rnd((1, 2, 4, 8), 50), rnd((1, 2, 1, 8), 51), rnd((1, 2, 1, 8), 52)
+    o, lse = oracle.attention(q, k, v, 0.7)
+    close(o, np.broadcast_to(v, o.shape))
+    s = 0.7 * np.einsum("bhid,bhjd->bhij", q, k)[..., 0]
+    close(lse, s)
+
+
+def test_causal_row_zero_sees_only_key_zero():
+    q, k, v = rnd((1, 1, 6, 4), 53), rnd((1, 1, 6, 4), 54), rnd((1, 1, 6, 4), 55)
+    o, lse = oracle.attention(q, k, v, 1.0, "causal")
+    close(o[0, 0, 0], v[0, 0, 0])
+    close(lse[0, 0, 0], float(q[0, 0, 0] @ k[0, 0, 0]))
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 3)])
+def test_zero_scores_average_visible_values(mask, window):
+    q, k, v = rnd((1, 1, 9, 4), 56), rnd((1, 1, 9, 4), 57), rnd((1, 1, 9, 4), 58)
+    for qq, sc in [(np.zeros_like(q), 1.0), (q, 0.0)]:
+        o, lse = oracle.attention(qq, k, v, sc, mask, window)
+        vis = A.visible_mask(np.arange(9), np.arange(9), mask, window)
+        for i in range(9):
+            close(o[0, 0, i], v[0, 0, vis[i]].mean(axis=0))
+            close(lse[0, 0, i], math.log(vis[i].sum()))
+
+
+def test_constant_values_give_constant_output():
+    q, k = rnd((1, 2, 12, 8), 59), rnd((1, 2, 12, 8), 60)
+    o, _ = oracle.attention(q, k, np.ones((1, 2, 12, 8)), 0.9, "sliding", window=4, rope_base=10000.0)
+    close(o, np.ones_like(o))
+
+
+def test_window_one_is_diagonal_and_wide_window_is_causal():
+    q, k, v = rnd((1, 1, 10, 4), 61), rnd((1, 1, 10, 4), 62), rnd((1, 1, 10, 4), 63)
+    o1, _ = oracle.attention(q, k, v, 1.0, "sliding", window=1)
+    close(o1, v)
+    ow, lw = oracle.attention(q, k, v, 1.0, "sliding", window=10)
+    oc, lc = oracle.attention(q, k, v, 1.0, "causal")
+    close(ow, oc)
+    close(lw, lc)
+
+
+def test_fully_masked_rows_are_zero_with_neg_inf_lse():
+    q, k, v = rnd((1, 1, 6, 4), 64), rnd((1, 1, 3, 4), 65), rnd((1, 1, 3, 4), 66)
+    o, lse = oracle.attention(q, k, v, 1.0, "causal")   # p_i = i - 3
+    assert np.all(o[0, 0, :3] == 0) and np.all(lse[0, 0, :3] == -np.inf)
+    assert np.all(np.isfinite(lse[0, 0, 3:]))
+
+
+def test_safe_softmax_survives_huge_scores():
+    """Append one dimension carrying a constant c: every score of a row moves by c*scale.
+
+    O must not change and LSE moves by exactly c*scale, with c large enough
+    that an unshifted exp would overflow to inf.
+    """
+    q, k, v = rnd((1, 1, 8, 4), 67), rnd((1, 1, 8, 4), 68), rnd((1, 1, 8, 4), 69)
+    o, lse = oracle.attention(q, k, v, 0.5, "causal")
+    c = 4000.0
+    qe = np.concatenate([q, np.full((1, 1, 8, 1), c)], axis=-1)
+    ke = np.concatenate([k, np.ones((1, 1, 8, 1))], axis=-1)
+    ve = np.concatenate([v, np.zeros((1, 1, 8, 1))], axis=-1)
+    o2, lse2 = oracle.attention(qe, ke, ve, 0.5, "causal")
+    close(o2[..., :4], o, rtol=1e-9, atol=1e-12)
+    close(lse2 - 0.5 * c, lse, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_position_zero_is_identity_and_norm_preserved():
+    x = rnd((1, 5, 16), 70)
+    close(oracle.rope_rotate(x[:, :1], np.array([0]), 10000.0), x[:, :1], rtol=0, atol=0)
+    r = oracle.rope_rotate(x, np.arange(5) * 37, 10000.0)
+    n_in = x[..., :8] ** 2 + x[..., 8:] ** 2
+    n_out = r[..., :8] ** 2 + r[..., 8:] ** 2
+    close(n_out, n_in)
+
+
+def test_rope_d2_is_plane_rotation():
+    for pos in [0, 1, 5, 1234]:
+        r = oracle.rope_rotate(np.array([[1.0, 0.0], [0.0, 1.0]]), np.array([pos, pos]), 10000.0)
+        close(r, [[math.cos(pos), math.sin(pos)], [-math.sin(pos), math.cos(pos)]], atol=1e-15)
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    q, k = rnd((1, 16), 71), rnd((1, 16), 72)
+    for base in [10000.0, 50.0]:
+        s = []
+        for shift in [0, 3, 1000]:
+            qr = oracle.rope_rotate(q, np.array([7 + shift]), base)
+            kr = oracle.rope_rotate(k, np.array([2 + shift]), base)
+            s.append(float(qr[0] @ kr[0]))
+        np.testing.assert_allclose(s, s[0], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- GQA
+def test_gqa_equals_mha_on_repeated_kv():
+    q, k, v = rnd((2, 8, 5, 8), 80), rnd((2, 2, 9, 8), 81), rnd((2, 2, 9, 8), 82)
+    o, lse = oracle.attention(q, k, v, 0.3, "causal", rope_base=10000.0)
+    kr, vr = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    o2, lse2 = oracle.attention(q, kr, vr, 0.3, "causal", rope_base=10000.0)
+    close(o, o2)
+    close(lse, lse2)
+
+
+# ---------------------------------------------------------------- library routine
+@pytest.mark.parametrize("mask,window,Nq,Nk", [("none", 0, 17, 23), ("causal", 0, 31, 31),
+                                               ("causal", 0, 9, 20), ("sliding", 6, 25, 25)])
+def test_matches_torch_sdpa_float64(mask, window, Nq, Nk):
+    q, k, v = rnd((2, 3, Nq, 16), 90), rnd((2, 3, Nk, 16), 91), rnd((2, 3, Nk, 16), 92)
+    scale = 0.21
+    o, lse = oracle.attention(q, k, v, scale, mask, window)
+    vis = A.visible_mask(A.query_positions(Nq, Nk), np.arange(Nk), mask, window)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    tm = torch.from_numpy(vis)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=scale)
+    s = (tq @ tk.transpose(-1, -2)) * scale
+    ref_lse = torch.logsumexp(s.masked_fill(~tm, -math.inf), dim=-1)
+    close(o, ref.numpy(), rtol=1e-11, atol=1e-13)
+    close(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_oracle_consumes_low_precision_inputs_exactly():
+    from workloads import gen_qkv
+    q, k, v = gen_qkv(1, 2, 2, 16, 16, 8, "bf16", seed=7)
+    o1, l1 = oracle.attention(q, k, v, 0.25, "causal")
+    o2, l2 = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.25, "causal")
+    close(o1, o2, rtol=0, atol=0)
+    close(l1, l2, rtol=0, atol=0)

@@ -1,0 +1,103 @@
+"""Seeded synthetic inputs shared by the HIP path's tests, the benchmark and the oracle.
+
+This module only draws random numbers and describes workload shapes. It holds
+none of the attention arithmetic: no scores, no softmax, no rotation, no merge.
+Both the fp64 oracle and the HIP kernels consume exactly the tensors produced
+here, so that input quantisation is never counted as kernel error.
+
+Recipe (one CPU generator per workload, seed fixed in advance):
+  q, then k, then v are drawn in that order as float32 N(0, 1) from
+  ``torch.Generator().manual_seed(seed)`` and cast with round-to-nearest-even
+  to the workload's dtype.  Layout is contiguous [B, H, N, D] row-major.
+
+The shapes follow the workloads the pages measure on: the AttnFuse listing's
+causal forward at B=4 H=12 N=4096 D=64 fp16 (its Tables 1-3), its RoPE+causal
+and sliding-window (W=256) variants (Tables 2, 4, 6, 7), and its flash-decoding
+geometry of 32 query heads sharing 8 KV heads of width 128 (Table 8), plus a
+tiny fp32 single-head case that the oracle finishes in well under a second.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal"]
+
+_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    D: int
+    dtype: str          # "f32" | "f16" | "bf16"
+    scale: float
+    mask: str           # "none" | "causal" | "sliding"
+    window: int = 0
+    rope_base: float = 0.0
+    num_splits: int = 0  # >0: split-KV decode with this many chunks
+    seed: int = 0
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _DT[self.dtype]
+
+    def shapes(self):
+        return ((self.B, self.Hq, self.Nq, self.D),
+                (self.B, self.Hkv, self.Nk, self.D),
+                (self.B, self.Hkv, self.Nk, self.D))
+
+
+WORKLOADS = [
+    Workload("tiny_dense_f32_n256_d64", B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64,
+             dtype="f32", scale=1.0 / math.sqrt(64), mask="none", seed=1),
+    Workload("causal_f16_b4h12_n4096_d64", B=4, Hq=12, Hkv=12, Nq=4096, Nk=4096, D=64,
+             dtype="f16", scale=1.0 / 8.0, mask="causal", seed=2),
+    Workload("rope_causal_f16_b4h12_n2048_d64", B=4, Hq=12, Hkv=12, Nq=2048, Nk=2048, D=64,
+             dtype="f16", scale=1.0 / 8.0, mask="causal", rope_base=10000.0, seed=3),
+    Workload("sliding256_bf16_b8h16_n8192_d128", B=8, Hq=16, Hkv=16, Nq=8192, Nk=8192, D=128,
+             dtype="bf16", scale=1.0 / math.sqrt(128), mask="sliding", window=256, seed=4),
+    Workload("gqa_decode_bf16_b16_32q8kv_nk32768_d128", B=16, Hq=32, Hkv=8, Nq=1, Nk=32768,
+             D=128, dtype="bf16", scale=1.0 / math.sqrt(128), mask="none", num_splits=64,
+             seed=5),
+]
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def gen_normal(shape, dtype: torch.dtype, gen: torch.Generator) -> torch.Tensor:
+    """float32 N(0,1) draw, then a round-to-nearest-even cast to ``dtype``."""
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    return x.to(dtype) if dtype != torch.float32 else x
+
+
+def gen_qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed):
+    """Draw (q, k, v) on the CPU in the fixed order q, k, v.
+
+    ``dtype`` is a torch dtype or one of "f32", "f16", "bf16".
+    Returns contiguous CPU tensors of shapes [B,Hq,Nq,D], [B,Hkv,Nk,D], [B,Hkv,Nk,D].
+    """
+    if isinstance(dtype, str):
+        dtype = _DT[dtype]
+    g = torch.Generator().manual_seed(int(seed))
+    q = gen_normal((B, Hq, Nq, D), dtype, g)
+    k = gen_normal((B, Hkv, Nk, D), dtype, g)
+    v = gen_normal((B, Hkv, Nk, D), dtype, g)
+    return q, k, v
+
+
+def gen_workload(w: Workload, seed: int | None = None):
+    return gen_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, w.torch_dtype,
+                   w.seed if seed is None else seed)
