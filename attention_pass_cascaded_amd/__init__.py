@@ -1,0 +1,21 @@
+"""Single-pass fused cascaded-reduction attention for AMD MI355X (gfx950).
+
+The product is the C-ABI library ``librfattn.so`` (``include/rf_attn.h``),
+built from the HIP sources in ``csrc/``.  This package is its thin Python
+binding: ``fwd``, ``splitkv_fwd``, ``lse_merge`` and ``decode`` marshal torch
+tensors (device memory and the current stream) into the C calls.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    RFError,
+    decode,
+    fwd,
+    load_library,
+    lse_merge,
+    splitkv_fwd,
+    workspace_bytes,
+)
+
+__all__ = ["fwd", "splitkv_fwd", "lse_merge", "decode", "workspace_bytes", "load_library",
+           "RFError", "LIB_PATH", "EXPORTED"]

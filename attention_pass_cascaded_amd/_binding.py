@@ -1,0 +1,156 @@
+"""ctypes binding to librfattn.so, with the same entry points as include/rf_attn.h.
+
+This layer only marshals arguments: it checks tensor placement, dtype and
+contiguity, allocates outputs with torch on the input's device, and passes raw
+device pointers plus the current HIP stream.  Every step of the computation
+runs in the HIP kernels.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librfattn.so")
+
+RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP = 0, 1, 2, 3
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_MASK = {"none": 0, "causal": 1, "sliding": 2}
+
+EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_splitkv_workspace_bytes",
+            "rf_lse_merge", "rf_status_string", "rf_last_error")
+
+
+class RFError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"rf_attn status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the built library is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m attention_pass_cascaded_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.rf_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, i, vp]
+    lib.rf_attn_fwd.restype = i
+    lib.rf_attn_splitkv_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, i, i, vp]
+    lib.rf_attn_splitkv_fwd.restype = i
+    lib.rf_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.rf_splitkv_workspace_bytes.restype = sz
+    lib.rf_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    lib.rf_lse_merge.restype = i
+    lib.rf_status_string.argtypes = [i]
+    lib.rf_status_string.restype = ctypes.c_char_p
+    lib.rf_last_error.argtypes = []
+    lib.rf_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != RF_OK:
+        lib = load_library()
+        raise RFError(status, lib.rf_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, D] tensor")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k and v must share one dtype")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, Hq, Nq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    return B, Hq, k.shape[1], Nq, k.shape[2], D
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def fwd(q, k, v, scale=None, mask="none", window=0, rope_base=0.0, out=None, lse=None):
+    """Fused forward.  Returns (o [B,Hq,Nq,D] in q.dtype, lse [B,Hq,Nq] float32)."""
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    _check(lib.rf_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, D,
+                           _scale(scale, D), _MASK[mask], int(window), float(rope_base),
+                           _DTYPE[q.dtype], _stream(q)))
+    return out, lse
+
+
+def workspace_bytes(B, Hq, Nq, D, num_splits) -> int:
+    return int(load_library().rf_splitkv_workspace_bytes(B, Hq, Nq, D, num_splits))
+
+
+def splitkv_fwd(q, k, v, num_splits, scale=None, mask="none", window=0, rope_base=0.0,
+                o_part=None, lse_part=None):
+    """Split-KV partials: (o_part [B,Hq,Nq,S,D] float32, lse_part [B,Hq,Nq,S] float32)."""
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
+    S = int(num_splits)
+    if o_part is None:
+        o_part = torch.empty((B, Hq, Nq, S, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, Nq, S), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    _check(lib.rf_attn_splitkv_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part),
+                                   B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask], int(window),
+                                   float(rope_base), S, _DTYPE[q.dtype], _stream(q)))
+    return o_part, lse_part
+
+
+def lse_merge(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
+    """Merge partials along the chunk axis: o_part [..., S, D], lse_part [..., S]."""
+    if not (o_part.is_cuda and lse_part.is_cuda and o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("o_part and lse_part must be contiguous GPU tensors")
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("partials are float32")
+    S, D = o_part.shape[-2], o_part.shape[-1]
+    lead = tuple(o_part.shape[:-2])
+    if tuple(lse_part.shape) != lead + (S,):
+        raise ValueError("lse_part must be o_part.shape[:-1]")
+    rows = math.prod(lead)
+    if out is None:
+        out = torch.empty(lead + (D,), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty(lead, dtype=torch.float32, device=o_part.device)
+    lib = load_library()
+    _check(lib.rf_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), rows, S, D,
+                            _DTYPE[out.dtype], _stream(o_part)))
+    return out, lse
+
+
+def decode(q, k, v, num_splits=64, scale=None, mask="none", window=0, rope_base=0.0):
+    """Split-KV attention: partials then log-sum-exp merge.  Returns (o, lse) like fwd."""
+    op, lp = splitkv_fwd(q, k, v, num_splits, scale, mask, window, rope_base)
+    return lse_merge(op, lp, out_dtype=q.dtype)

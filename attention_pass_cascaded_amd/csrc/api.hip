@@ -1,0 +1,183 @@
+// Host side of the C ABI declared in include/rf_attn.h: argument validation,
+// choice of kernel, launches on the caller's stream, status codes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "launch.hpp"
+#include "merge_kernel.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rf_status fail(rf_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+rf_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return RF_OK;
+    return fail(RF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Shared validation of the attention arguments.  Fills p on success.
+rf_status check_attn(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int Nq,
+                     int Nk, int D, float scale, int mask_kind, int window, float rope_base,
+                     int dtype, rf::AttnParams& p) {
+    if (B < 0 || Nq < 0 || Nk < 0) return fail(RF_ERR_INVALID_ARG, "negative size (B=%d Nq=%d Nk=%d)", B, Nq, Nk);
+    if (Hq < 1 || Hkv < 1) return fail(RF_ERR_INVALID_ARG, "Hq and Hkv must be >= 1 (Hq=%d Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv) return fail(RF_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (dtype != RF_F32 && dtype != RF_F16 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (mask_kind != RF_MASK_NONE && mask_kind != RF_MASK_CAUSAL && mask_kind != RF_MASK_SLIDING)
+        return fail(RF_ERR_INVALID_ARG, "unknown mask kind %d", mask_kind);
+    if (mask_kind == RF_MASK_SLIDING && window < 1)
+        return fail(RF_ERR_INVALID_ARG, "sliding window needs window >= 1 (got %d)", window);
+    if (!isfinite(scale) || scale < 0.f) return fail(RF_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    if (isnan(rope_base) || isinf(rope_base)) return fail(RF_ERR_INVALID_ARG, "rope_base must be finite");
+    if (D != 64 && D != 128) return fail(RF_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+    const bool q_nonempty = (size_t)B * Nq > 0;
+    const bool kv_nonempty = (size_t)B * Nk > 0;
+    if (q_nonempty && !q) return fail(RF_ERR_INVALID_ARG, "q is null");
+    if (kv_nonempty && (!k || !v)) return fail(RF_ERR_INVALID_ARG, "k or v is null");
+    if ((q && !aligned16(q)) || (k && !aligned16(k)) || (v && !aligned16(v)))
+        return fail(RF_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+    if ((size_t)B * Hq > (size_t)1 << 30) return fail(RF_ERR_INVALID_ARG, "B*Hq too large");
+    p = rf::AttnParams{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.D = D;
+    p.scale = scale;
+    p.mask = mask_kind;
+    p.window = mask_kind == RF_MASK_SLIDING ? window : 0;
+    p.rope_base = rope_base > 0.f ? rope_base : 0.f;
+    p.num_splits = 1;
+    p.split_len = Nk;
+    return RF_OK;
+}
+
+hipError_t launch_fwd(const rf::AttnParams& p, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case RF_F32: return rf::launch_fwd_f32(p, s);
+        case RF_F16: return rf::launch_fwd_f16(p, s);
+        default: return rf::launch_fwd_bf16(p, s);
+    }
+}
+
+hipError_t launch_decode(const rf::AttnParams& p, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case RF_F32: return rf::launch_decode_f32(p, s);
+        case RF_F16: return rf::launch_decode_f16(p, s);
+        default: return rf::launch_decode_bf16(p, s);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int D, float scale, int mask_kind, int window,
+                      float rope_base, int dtype, hipStream_t stream) {
+    rf::AttnParams p;
+    rf_status st = check_attn(q, k, v, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base, dtype, p);
+    if (st != RF_OK) return st;
+    if ((size_t)B * Nq == 0) return RF_OK;
+    if (!o || !lse) return fail(RF_ERR_INVALID_ARG, "o and lse are required");
+    if (!aligned16(o) || ((uintptr_t)lse & 3u)) return fail(RF_ERR_INVALID_ARG, "o must be 16-byte aligned, lse 4-byte aligned");
+    if ((Nq + rf::FWD_BM - 1) / rf::FWD_BM > 65535) return fail(RF_ERR_INVALID_ARG, "Nq too large");
+    p.o = o;
+    p.lse = lse;
+    return hip_status(launch_fwd(p, dtype, stream), "rf_attn_fwd launch");
+}
+
+size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits) {
+    if (B < 0 || Hq < 1 || Nq < 0 || D < 1 || num_splits < 1) return 0;
+    return (size_t)B * Hq * Nq * num_splits * (size_t)(D + 1) * sizeof(float);
+}
+
+rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale, int mask_kind,
+                              int window, float rope_base, int num_splits, int dtype, hipStream_t stream) {
+    rf::AttnParams p;
+    rf_status st = check_attn(q, k, v, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base, dtype, p);
+    if (st != RF_OK) return st;
+    if (num_splits < 1 || num_splits > 4096) return fail(RF_ERR_INVALID_ARG, "num_splits must be in [1, 4096] (got %d)", num_splits);
+    if ((size_t)B * Nq == 0) return RF_OK;
+    if (!o_part || !lse_part) return fail(RF_ERR_INVALID_ARG, "o_part and lse_part are required");
+    if (!aligned16(o_part) || ((uintptr_t)lse_part & 3u))
+        return fail(RF_ERR_INVALID_ARG, "o_part must be 16-byte aligned, lse_part 4-byte aligned");
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.num_splits = num_splits;
+    p.split_len = (Nk + num_splits - 1) / num_splits;
+    p.split_mode = 1;
+    const int rows = (Hq / Hkv) * Nq;
+    if (rows <= rf::DEC_MAX_ROWS && Hkv <= 65535 && B <= 65535)
+        return hip_status(launch_decode(p, dtype, stream), "rf_attn_splitkv_fwd decode launch");
+    if ((Nq + rf::FWD_BM - 1) / rf::FWD_BM > 65535) return fail(RF_ERR_INVALID_ARG, "Nq too large");
+    if ((size_t)B * Hq * num_splits > 0x7fffffffu) return fail(RF_ERR_INVALID_ARG, "B*Hq*num_splits too large");
+    return hip_status(launch_fwd(p, dtype, stream), "rf_attn_splitkv_fwd launch");
+}
+
+rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int rows,
+                       int num_splits, int D, int out_dtype, hipStream_t stream) {
+    if (rows < 0) return fail(RF_ERR_INVALID_ARG, "rows must be >= 0");
+    if (num_splits < 1 || num_splits > 4096) return fail(RF_ERR_INVALID_ARG, "num_splits must be in [1, 4096]");
+    if (out_dtype != RF_F32 && out_dtype != RF_F16 && out_dtype != RF_BF16)
+        return fail(RF_ERR_INVALID_ARG, "unknown dtype %d", out_dtype);
+    if (D != 64 && D != 128) return fail(RF_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+    if (rows == 0) return RF_OK;
+    if (!o_part || !lse_part || !o || !lse) return fail(RF_ERR_INVALID_ARG, "null pointer");
+    if (((uintptr_t)o_part & 3u) || ((uintptr_t)lse_part & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)o & 3u))
+        return fail(RF_ERR_INVALID_ARG, "misaligned pointer");
+    return hip_status(rf::launch_merge(o_part, lse_part, o, lse, rows, num_splits, D, out_dtype, stream),
+                      "rf_lse_merge launch");
+}
+
+const char* rf_status_string(rf_status s) {
+    switch (s) {
+        case RF_OK: return "ok";
+        case RF_ERR_INVALID_ARG: return "invalid argument";
+        case RF_ERR_UNSUPPORTED: return "unsupported";
+        case RF_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* rf_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+namespace rf {
+
+template <typename T, int D>
+static hipError_t merge_one(const float* op, const float* lp, void* o, float* lse, int rows, int S, hipStream_t s) {
+    dim3 grid((unsigned)((rows + MRG_ROWS - 1) / MRG_ROWS));
+    hipLaunchKernelGGL((lse_merge_kernel<T, D>), grid, dim3(MRG_THREADS), 0, s, op, lp, (T*)o, lse, rows, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* op, const float* lp, void* o, float* lse, int rows, int S, int D, int dtype,
+                        hipStream_t s) {
+    if (dtype == RF_F32) return D == 64 ? merge_one<float, 64>(op, lp, o, lse, rows, S, s) : merge_one<float, 128>(op, lp, o, lse, rows, S, s);
+    if (dtype == RF_F16) return D == 64 ? merge_one<_Float16, 64>(op, lp, o, lse, rows, S, s) : merge_one<_Float16, 128>(op, lp, o, lse, rows, S, s);
+    return D == 64 ? merge_one<__bf16, 64>(op, lp, o, lse, rows, S, s) : merge_one<__bf16, 128>(op, lp, o, lse, rows, S, s);
+}
+
+}  // namespace rf

@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// MFMA wrappers, conversions and the per-call launch parameters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rf_attn.h"
+
+namespace rf {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Fused forward work-group: 4 wavefronts of 32 query rows each.
+constexpr int FWD_WAVES = 4;
+constexpr int FWD_THREADS = 64 * FWD_WAVES;
+constexpr int FWD_BM = 32 * FWD_WAVES;  // query rows per work-group
+
+// Everything a launch needs, filled and validated on the host.
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;           // final output (input dtype), or null in split mode
+    float* lse;        // final lse, or null in split mode
+    float* o_part;     // split mode: [B, Hq, Nq, S, D] float32
+    float* lse_part;   // split mode: [B, Hq, Nq, S] float32
+    int B, Hq, Hkv, Nq, Nk, D;
+    float scale;
+    int mask;          // rf_mask
+    int window;
+    float rope_base;   // > 0: RoPE on
+    int num_splits;    // 1 when not splitting
+    int split_len;     // keys per chunk, ceil(Nk / num_splits)
+    int split_mode;    // 1: write normalised partials + chunk lse
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Elements of T packed into 16 bytes.
+template <typename T> struct Vec16;
+template <> struct Vec16<_Float16> { typedef f16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<__bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
+
+// 32x32 output tile, float32 accumulate.  16-bit inputs: 16-deep contraction,
+// lane l holds row/column (l % 32) and 8 consecutive contraction slots
+// 8*(l/32)..+7 of each operand.  float32 inputs: 2-deep, one slot (l/32).
+// Output register j of lane l is element [8*(j/4) + 4*(l/32) + j%4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Exchange with the lane 32 away (the other half of the wavefront).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// RoPE angle of frequency i at integer position pos, returned as (cos, sin).
+// inv_period = theta_i / (2*pi) is kept in double so the product with large
+// positions keeps its fraction; v_sin/v_cos take revolutions in [0, 1).
+__device__ __forceinline__ void rope_cos_sin(double inv_period, int pos, float& c, float& s) {
+    double r = (double)pos * inv_period;
+    r = r - floor(r);
+    float rf = (float)r;
+    c = __builtin_amdgcn_cosf(rf);
+    s = __builtin_amdgcn_sinf(rf);
+}
+
+// theta_i / (2 pi) with theta_i = base^(-2 i / D).
+__device__ __forceinline__ double rope_inv_period(float base, int i, int D) {
+    const double inv_two_pi = 0.15915494309189533576888;
+    return exp2(-2.0 * (double)i / (double)D * log2((double)base)) * inv_two_pi;
+}
+
+}  // namespace rf

@@ -1,0 +1,420 @@
+// Fused single-pass attention forward for gfx950 (MFMA).
+//
+// The cascade max -> exp-sum -> P.V ("RedFuser", abstract and Fig. 3) runs in
+// its incremental form (RedFuser Fig. 4b): each key tile updates a running
+// (m, l, O) per query row, so on-chip state is constant in the key length.
+// The scores use the max/+ pair and the output the +/* pair of RedFuser
+// Table 1; rescaling by 2^(m_old - m_new) is what lets max distribute over +.
+// Variants: pre-matmul RoPE on Q and K (AttnFuse abstract, Fig. 1), causal and
+// sliding-window visibility (AttnFuse Table 6), GQA head sharing and split-KV
+// partials (RedFuser Fig. 13, AttnFuse Table 8).
+//
+// Work-group: 4 wavefronts, 128 query rows (32 per wave), one (batch, head,
+// key chunk).  Per key tile of BN keys:
+//   S^T = K . Q^T on MFMA 32x32 (A = K tile from LDS, B = Q^T held in
+//   registers), so lane l owns query row (l % 32) and 16 keys per 32-key
+//   block: the row max and row sum are in-lane plus one swap between the two
+//   32-lane halves.
+//   O^T += V^T . P^T on MFMA 32x32 (A = V^T from LDS, B = P^T straight from
+//   the score registers), so the rescale of O by alpha is a per-lane scalar.
+// K is staged row-major in LDS; V is written transposed (d-major) with the key
+// slots permuted so each lane's 8 contraction slots are 16 contiguous bytes.
+// K/V tiles are double-buffered: the global loads of tile t+1 are issued
+// before the math of tile t and written to LDS after it (one barrier a tile).
+#pragma once
+
+#include "common.hpp"
+
+namespace rf {
+
+// SPLITK: K (and Q) are kept as a bf16 hi/lo pair, x = hi + lo, so rotated
+// operands keep ~16 mantissa bits; S then takes three MFMAs (hi.hi, hi.lo,
+// lo.hi).  Used for bf16 with RoPE, where rounding the rotated q and k to a
+// single bf16 dominates the output error.
+template <typename T, int D, bool SPLITK = false>
+struct FwdCfg {
+    static constexpr bool F32 = sizeof(T) == 4;
+    static constexpr int BN = F32 ? 32 : 64;            // keys per tile
+    static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
+    static constexpr int CPR = D / EPC;                 // chunks per row
+    static constexpr int KSTRIDE = D + EPC;             // K row pitch (elements), +16 B
+    static constexpr int VROWS = F32 ? BN : D;          // f32 keeps V row-major
+    static constexpr int VSTRIDE = F32 ? D + EPC : BN + 8;
+    static constexpr int K_ELEMS = BN * KSTRIDE * (SPLITK ? 2 : 1);  // hi tile, then lo tile
+    static constexpr int STAGE = K_ELEMS + VROWS * VSTRIDE;
+    static constexpr int CH = BN * CPR / FWD_THREADS;   // 16-byte chunks per thread per tile
+    static constexpr int RPW = 64 / CPR;                // key rows one wave covers per chunk
+    static_assert(CH >= 2 && CH % 2 == 0, "tile must give each thread an even chunk count");
+};
+
+// Key slot inside a 16-bit V^T tile: bits 2 and 3 of the key index swapped.
+// MFMA output register j of lane-half h holds key 8*(j/4) + 4*h + j%4 of its
+// 32-key block; feeding registers 8t..8t+7 as one B operand makes contraction
+// slot (h, i) key 16t + 8*(i/4) + 4*h + i%4, which this swap stores at
+// 16t + 8*h + i.
+__device__ __forceinline__ int vt_slot(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <typename T, int D, bool ROPE>
+__global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) {
+    constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
+    using C = FwdCfg<T, D, SPLITK>;
+    constexpr bool F32 = C::F32;
+    constexpr int BN = C::BN;
+    constexpr int EPC = C::EPC;
+    constexpr int CPR = C::CPR;
+    constexpr int NKB = BN / 32;      // 32-key blocks per tile
+    constexpr int NDB = D / 32;       // 32-wide d blocks of the output
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr float LN2 = 0.6931471805599453f;
+    typedef typename Vec16<T>::type VecT;
+
+    __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    // x = (b * Hq + h) * S + split; y = query block, heaviest (latest) first
+    int bx = blockIdx.x;
+    const int split = bx % p.num_splits;
+    bx /= p.num_splits;
+    const int h = bx % p.Hq;
+    const int b = bx / p.Hq;
+    const int qb = gridDim.y - 1 - blockIdx.y;
+    const int q0 = qb * FWD_BM;
+    const int g = h / (p.Hq / p.Hkv);
+    const int pos_off = p.Nk - p.Nq;
+
+    // Key range the whole work-group visits.
+    const int last_row = min(p.Nq, q0 + FWD_BM) - 1;
+    int klo = split * p.split_len;
+    int khi = min(p.Nk, klo + p.split_len);
+    if (p.mask != RF_MASK_NONE) khi = min(khi, last_row + pos_off + 1);
+    if (p.mask == RF_MASK_SLIDING) klo = max(klo, q0 + pos_off - p.window + 1);
+    const int ntiles = khi > klo ? (khi - klo + BN - 1) / BN : 0;
+
+    // This wave's rows and their positions.
+    const int wrow0 = q0 + 32 * wave;
+    const bool wave_live = wrow0 < p.Nq;
+    const int pw_min = wrow0 + pos_off;
+    const int pw_max = min(p.Nq, wrow0 + 32) - 1 + pos_off;
+    const int my_row = wrow0 + l32;
+    const int my_pos = my_row + pos_off;
+
+    const float c = p.scale * LOG2E;
+    const size_t kv_base = ((size_t)b * p.Hkv + g) * (size_t)p.Nk * D;
+    const T* __restrict__ kg = (const T*)p.k + kv_base;
+    const T* __restrict__ vg = (const T*)p.v + kv_base;
+
+    // ---------------- Q^T operand (+ RoPE), loaded once
+    // lane element n in [0, D/2): d(n) = 16*(n/8) + 8*hi + n%8 (16-bit)
+    //                                   = 2*n + hi               (f32)
+    // its rotation partner d(n) + D/2 is element n + D/4 of the same lane.
+    constexpr int QN = D / 2;
+    float qf[QN];
+    {
+        const T* qrow = (const T*)p.q + (((size_t)b * p.Hq + h) * p.Nq + (size_t)my_row) * D;
+        const bool ok = my_row < p.Nq;
+#pragma unroll
+        for (int n = 0; n < QN; ++n) {
+            const int d = F32 ? 2 * n + hi : 16 * (n / 8) + 8 * hi + (n % 8);
+            qf[n] = ok ? to_f32(qrow[d]) : 0.f;
+        }
+        if (ROPE) {
+#pragma unroll
+            for (int n = 0; n < QN / 2; ++n) {
+                const int d = F32 ? 2 * n + hi : 16 * (n / 8) + 8 * hi + (n % 8);
+                float cs, sn;
+                rope_cos_sin(rope_inv_period(p.rope_base, d, D), my_pos, cs, sn);
+                const float x = qf[n], y = qf[n + QN / 2];
+                qf[n] = x * cs - y * sn;
+                qf[n + QN / 2] = x * sn + y * cs;
+            }
+        }
+    }
+    constexpr int NKS = F32 ? D / 2 : D / 16;  // contraction steps over d
+    VecT qv[F32 ? 1 : NKS];
+    VecT qlo[SPLITK ? NKS : 1];
+    float qs[F32 ? NKS : 1];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (F32) {
+            qs[ks] = qf[ks];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qv[ks][i] = from_f32<T>(qf[8 * ks + i]);
+                if constexpr (SPLITK) qlo[ks][i] = from_f32<T>(qf[8 * ks + i] - to_f32(qv[ks][i]));
+            }
+        }
+    }
+
+    // ---------------- RoPE constants for this thread's K chunks
+    // With RoPE the thread loads chunk cc and its partner cc + CPR/2 of a row.
+    double ipd[ROPE ? EPC : 1];
+    if (ROPE) {
+        const int cc = tid % (CPR / 2);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ipd[e] = rope_inv_period(p.rope_base, cc * EPC + e, D);
+    }
+
+    // ---------------- tile staging
+    uint4 kreg[C::CH], vreg[C::CH];
+
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int it = 0; it < C::CH; ++it) {
+            int row, ch;
+            if (ROPE) {  // pairs (cc, cc + CPR/2)
+                const int u = (it / 2) * FWD_THREADS + tid;
+                row = u / (CPR / 2);
+                ch = u % (CPR / 2) + (it % 2) * (CPR / 2);
+            } else {
+                const int u = it * FWD_THREADS + tid;
+                row = u / CPR;
+                ch = u % CPR;
+            }
+            const int key = k0 + row;
+            kreg[it] = key < p.Nk ? *(const uint4*)(kg + (size_t)key * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < C::CH; ++it) {
+            int row, ch;
+            if (F32) {
+                const int u = it * FWD_THREADS + tid;
+                row = u / CPR;
+                ch = u % CPR;
+            } else {
+                const int slot = C::RPW * (it * FWD_WAVES + wave) + lane / CPR;
+                row = vt_slot(slot);
+                ch = lane % CPR;
+            }
+            const int key = k0 + row;
+            vreg[it] = key < p.Nk ? *(const uint4*)(vg + (size_t)key * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    auto store_tile = [&](int stage, int k0) {
+        T* ks_ = smem + stage * C::STAGE;
+        T* vs_ = ks_ + C::K_ELEMS;
+        if (ROPE) {
+#pragma unroll
+            for (int it = 0; it < C::CH; it += 2) {
+                const int u = (it / 2) * FWD_THREADS + tid;
+                const int row = u / (CPR / 2);
+                const int cc = u % (CPR / 2);
+                const int pos = k0 + row;
+                VecT lo = *(VecT*)&kreg[it];
+                VecT hi_ = *(VecT*)&kreg[it + 1];
+                VecT olo, ohi, rlo, rhi;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    float cs, sn;
+                    rope_cos_sin(ipd[e], pos, cs, sn);
+                    const float x = to_f32(lo[e]), y = to_f32(hi_[e]);
+                    const float xr = x * cs - y * sn, yr = x * sn + y * cs;
+                    olo[e] = from_f32<T>(xr);
+                    ohi[e] = from_f32<T>(yr);
+                    if constexpr (SPLITK) {
+                        rlo[e] = from_f32<T>(xr - to_f32(olo[e]));
+                        rhi[e] = from_f32<T>(yr - to_f32(ohi[e]));
+                    }
+                }
+                *(VecT*)(ks_ + row * C::KSTRIDE + cc * EPC) = olo;
+                *(VecT*)(ks_ + row * C::KSTRIDE + (cc + CPR / 2) * EPC) = ohi;
+                if constexpr (SPLITK) {
+                    T* kl = ks_ + BN * C::KSTRIDE;
+                    *(VecT*)(kl + row * C::KSTRIDE + cc * EPC) = rlo;
+                    *(VecT*)(kl + row * C::KSTRIDE + (cc + CPR / 2) * EPC) = rhi;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < C::CH; ++it) {
+                const int u = it * FWD_THREADS + tid;
+                *(uint4*)(ks_ + (u / CPR) * C::KSTRIDE + (u % CPR) * EPC) = kreg[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::CH; ++it) {
+            if constexpr (F32) {
+                const int u = it * FWD_THREADS + tid;
+                *(uint4*)(vs_ + (u / CPR) * C::VSTRIDE + (u % CPR) * EPC) = vreg[it];
+            } else {
+                const int slot = C::RPW * (it * FWD_WAVES + wave) + lane / CPR;
+                const int ch = lane % CPR;
+                VecT x = *(VecT*)&vreg[it];
+#pragma unroll
+                for (int e0 = 0; e0 < 8; ++e0) {
+                    const int e = (e0 + ch) & 7;  // stagger: lanes of one row hit different banks
+                    vs_[(ch * 8 + e) * C::VSTRIDE + slot] = x[e];
+                }
+            }
+        }
+    };
+
+    // ---------------- running state
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    if (ntiles > 0) {
+        load_tile(klo);
+        store_tile(0, klo);
+    }
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = klo + t * BN;
+        const int stage = t & 1;
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(k0 + BN);
+
+        // wave-level skip / mask decisions
+        bool skip = !wave_live;
+        bool need_mask = (k0 + BN > khi);
+        if (p.mask != RF_MASK_NONE) {
+            skip |= k0 > pw_max;
+            need_mask |= (k0 + BN - 1 > pw_min);
+            if (p.mask == RF_MASK_SLIDING) {
+                skip |= (k0 + BN - 1 <= pw_min - p.window);
+                need_mask |= (k0 <= pw_max - p.window);
+            }
+        }
+
+        if (!skip) {
+            const T* ks_ = smem + stage * C::STAGE;
+            const T* vs_ = ks_ + C::K_ELEMS;
+
+            // S^T = K . Q^T
+            f32x16 sacc[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                sacc[kb] = f32x16{};
+                const T* krow = ks_ + (32 * kb + l32) * C::KSTRIDE;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if constexpr (F32) {
+                        sacc[kb] = mfma32(krow[2 * ks + hi], qs[ks], sacc[kb]);
+                    } else {
+                        const VecT a = *(const VecT*)(krow + 16 * ks + 8 * hi);
+                        sacc[kb] = mfma32(a, qv[ks], sacc[kb]);
+                        if constexpr (SPLITK) {
+                            const VecT al = *(const VecT*)(krow + BN * C::KSTRIDE + 16 * ks + 8 * hi);
+                            sacc[kb] = mfma32(a, qlo[ks], sacc[kb]);
+                            sacc[kb] = mfma32(al, qv[ks], sacc[kb]);
+                        }
+                    }
+                }
+            }
+
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = k0 + 32 * kb + 8 * (j / 4) + 4 * hi + (j % 4);
+                        bool vis = key < khi;
+                        if (p.mask != RF_MASK_NONE) vis &= key <= my_pos;
+                        if (p.mask == RF_MASK_SLIDING) vis &= key > my_pos - p.window;
+                        if (!vis) sacc[kb][j] = -INFINITY;
+                    }
+            }
+
+            // level 1: running max (log2 domain of the scaled scores)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+            mx = fmaxf(mx, swap_halves(mx));
+            const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
+            const float m_new = fmaxf(m_run, m_tile);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_use);
+            m_run = m_new;
+
+            // level 2 and the correction of level 3
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+            float pr[NKB][16];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float e = fast_exp2(fmaf(sacc[kb][j], c, -m_use));
+                    if (need_mask) e = (sacc[kb][j] == -INFINITY) ? 0.f : e;
+                    pr[kb][j] = e;
+                    l_run += e;
+                }
+
+            // level 3: O^T += V^T . P^T
+            if constexpr (F32) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = 32 * kb + 8 * (j / 4) + 4 * hi + (j % 4);
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            oacc[db] = mfma32(vs_[key * C::VSTRIDE + 32 * db + l32], pr[kb][j], oacc[db]);
+                    }
+            } else {
+#pragma unroll
+                for (int t16 = 0; t16 < BN / 16; ++t16) {
+                    VecT pb;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pb[i] = from_f32<T>(pr[t16 / 2][8 * (t16 % 2) + i]);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const VecT a = *(const VecT*)(vs_ + (32 * db + l32) * C::VSTRIDE + 16 * t16 + 8 * hi);
+                        oacc[db] = mfma32(a, pb, oacc[db]);
+                    }
+                }
+            }
+        }
+
+        if (t + 1 < ntiles) store_tile(stage ^ 1, k0 + BN);
+    }
+
+    // ---------------- epilogue: O /= l, lse = ln sum exp
+    const float l_tot = l_run + swap_halves(l_run);
+    const bool live = l_tot > 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
+    const float lse_v = live ? (m_run + fast_log2(l_tot)) * LN2 : -INFINITY;
+    if (!wave_live || my_row >= p.Nq) return;
+    const size_t row_id = ((size_t)b * p.Hq + h) * p.Nq + (size_t)my_row;
+    if (p.split_mode) {
+        float* orow = p.o_part + (row_id * p.num_splits + split) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+                const int d0 = 32 * db + 8 * jq + 4 * hi;
+                float4 w = make_float4(oacc[db][4 * jq] * inv, oacc[db][4 * jq + 1] * inv,
+                                       oacc[db][4 * jq + 2] * inv, oacc[db][4 * jq + 3] * inv);
+                *(float4*)(orow + d0) = w;
+            }
+        if (hi == 0) p.lse_part[row_id * p.num_splits + split] = lse_v;
+    } else {
+        T* orow = (T*)p.o + row_id * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+                const int d0 = 32 * db + 8 * jq + 4 * hi;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) orow[d0 + r] = from_f32<T>(oacc[db][4 * jq + r] * inv);
+            }
+        if (hi == 0) p.lse[row_id] = lse_v;
+    }
+}
+
+}  // namespace rf

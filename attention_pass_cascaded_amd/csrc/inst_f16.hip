@@ -1,0 +1,3 @@
+// Kernel instances for float16 inputs.
+#include "instances.hpp"
+RF_DEFINE_LAUNCHERS(f16, _Float16)

@@ -1,0 +1,22 @@
+// Internal launchers, one translation unit per input dtype (built in parallel).
+#pragma once
+
+#include "common.hpp"
+
+namespace rf {
+
+// Fused forward, or split-KV partials when p.split_mode != 0 (MFMA path).
+hipError_t launch_fwd_f32(const AttnParams& p, hipStream_t s);
+hipError_t launch_fwd_f16(const AttnParams& p, hipStream_t s);
+hipError_t launch_fwd_bf16(const AttnParams& p, hipStream_t s);
+
+// Split-KV partials on the streaming decode kernel; needs (Hq/Hkv)*Nq <= DEC_MAX_ROWS.
+constexpr int DEC_MAX_ROWS = 8;
+hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
+hipError_t launch_decode_f16(const AttnParams& p, hipStream_t s);
+hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);
+
+hipError_t launch_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                        int rows, int S, int D, int dtype, hipStream_t s);
+
+}  // namespace rf

@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused cascaded-reduction attention on one MI355X.
+
+A step is one fused forward (rf_attn_fwd) over the causal fp16 prefill
+workload B=4 H=12 N=4096 D=64 (the workload the AttnFuse listing's Tables 1-3
+time on H100 NVL), inputs resident in HBM.  The split-KV decode (GQA 32q/8kv,
+D=128, 32768 cached keys, 64 chunks of 512; AttnFuse Table 8 geometry) and the
+other prefill variants are timed in the same run and reported as secondary
+objects.  Prints ONE JSON line.
+
+Work counted (algorithmic, not what the kernels happen to execute):
+  flops = 4 * D per visible (query, key) pair (Q.K^T and P.V, 2 each);
+  bytes = q, k, v read once + o written once (+ lse, float32).
+Timing: torch.cuda.Event on the stream the kernels are launched on (the
+current stream), W untimed warmup steps, then K timed steps back to back.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused attn-fwd TFLOP/s (prefill) + decode HBM GB/s, % of MI355X roofline"
+HEADLINE = "causal_f16_b4h12_n4096_d64"
+DECODE = "gqa_decode_bf16_b16_32q8kv_nk32768_d128"
+VARIANTS = ["rope_causal_f16_b4h12_n2048_d64", "sliding256_bf16_b8h16_n8192_d128"]
+
+# MI355X published peaks: 256 CUs at 2.4 GHz.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+# Files whose content defines each kernel: HBM counter figures are used only
+# while these are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "fwd": ["attention_pass_cascaded_amd/csrc/fwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "decode": ["attention_pass_cascaded_amd/csrc/decode_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+}
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(Nq: int, Nk: int, mask: str, window: int = 0) -> int:
+    """(query, key) pairs a head computes: query i at position Nk - Nq + i."""
+    total = 0
+    for i in range(Nq):
+        p = Nk - Nq + i
+        if mask == "none":
+            total += Nk
+        else:
+            hi = min(p, Nk - 1)
+            lo = 0 if mask == "causal" else max(0, p - window + 1)
+            total += max(0, hi - lo + 1)
+    return total
+
+
+def alg_flops(w) -> float:
+    return 4.0 * w.D * visible_pairs(w.Nq, w.Nk, w.mask, w.window) * w.B * w.Hq
+
+
+def alg_bytes(w) -> float:
+    es = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    qo = 2 * w.B * w.Hq * w.Nq * w.D * es
+    kv = 2 * w.B * w.Hkv * w.Nk * w.D * es
+    return float(qo + kv + 4 * w.B * w.Hq * w.Nq)
+
+
+def traffic_from_profiles(kind: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if still valid."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    hsh = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not hsh or hsh.group(1) != kernel_hash(kind):
+        return None
+    return float(m.group(1))
+
+
+def time_loop(fn, steps: int, warmup: int) -> float:
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def run_prefill(w, steps, warmup):
+    import torch
+    import attention_pass_cascaded_amd as rf
+    from workloads import gen_workload
+    q, k, v = gen_workload(w, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        rf.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, rope_base=w.rope_base, out=o, lse=lse)
+
+    ms = time_loop(step, steps, warmup)
+    flops = alg_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    byts = alg_bytes(w)
+    gbs = byts / (ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles("fwd", w.name)
+    res = {
+        "workload": w.name, "ms": ms, "TFLOP/s": tflops, "GB/s": gbs,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": traffic},
+        "hbm_frac": gbs / PEAK_HBM_GBS,
+        "alg_gflop": flops / 1e9, "alg_mb": byts / 1e6,
+    }
+    return res, (q, k, v)
+
+
+def run_decode(w, steps, warmup):
+    import torch
+    import attention_pass_cascaded_amd as rf
+    from workloads import gen_workload
+    q, k, v = gen_workload(w, device="cuda")
+    S = w.num_splits
+    op = torch.empty((w.B, w.Hq, w.Nq, S, w.D), dtype=torch.float32, device="cuda")
+    lp = torch.empty((w.B, w.Hq, w.Nq, S), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+
+    def part():
+        rf.splitkv_fwd(q, k, v, S, scale=w.scale, mask=w.mask, window=w.window, rope_base=w.rope_base,
+                       o_part=op, lse_part=lp)
+
+    def merge():
+        rf.lse_merge(op, lp, out_dtype=q.dtype, out=o, lse=lse)
+
+    def step():
+        part()
+        merge()
+
+    ms = time_loop(step, steps, warmup)
+    ms_part = time_loop(part, steps, warmup)
+    ms_merge = time_loop(merge, steps, warmup)
+    byts = alg_bytes(w)
+    gbs = byts / (ms * 1e-3) / 1e9
+    gbs_part = byts / (ms_part * 1e-3) / 1e9
+    traffic = traffic_from_profiles("decode", w.name)
+    return {
+        "workload": w.name, "value": gbs, "unit": "GB/s", "ms_per_step": ms,
+        "ms_partial_kernel": ms_part, "ms_merge_kernel": ms_merge,
+        "roofline": {"bound": "hbm", "achieved": gbs_part, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs_part / PEAK_HBM_GBS, "traffic": traffic},
+        "step_frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+        "alg_mb": byts / 1e6, "alg_gflop": alg_flops(w) / 1e9,
+    }
+
+
+def cpu_baseline(w, q, k, v, heads: int):
+    """The fp64 oracle on a bounded sample: batch 0, the first `heads` heads."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    qs = q[:1, :heads].cpu()
+    ks = k[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
+    vs = v[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
+    t0 = time.perf_counter()
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=cores):
+            oracle.attention(qs, ks, vs, w.scale, w.mask, w.window, w.rope_base)
+    else:
+        oracle.attention(qs, ks, vs, w.scale, w.mask, w.window, w.rope_base)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * visible_pairs(w.Nq, w.Nk, w.mask, w.window) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"batch 0, heads 0..{heads - 1} of {w.name} ({heads}/{w.B * w.Hq} of the workload, "
+                      f"{flops / 1e9:.2f} GFLOP) in {dt:.1f} s, float64 numpy"}
+
+
+def copy_calibration(nbytes: int, steps: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default=None, help="time a single workload (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import by_name
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
+
+    if args.only:
+        w = by_name(args.only)
+        res = run_decode(w, args.steps, args.warmup) if w.num_splits else run_prefill(w, args.steps, args.warmup)[0]
+        print(json.dumps(res), flush=True)
+        return
+
+    w = by_name(HEADLINE)
+    head, (q, k, v) = run_prefill(w, args.steps, args.warmup)
+    print(f"# headline {w.name}: {head['ms']:.4f} ms, {head['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    dec = run_decode(by_name(DECODE), max(5, args.steps // 2), max(2, args.warmup // 2))
+    print(f"# decode: {dec['ms_per_step']:.4f} ms, {dec['value']:.0f} GB/s", file=sys.stderr, flush=True)
+    variants = {}
+    for name in VARIANTS:
+        r, _ = run_prefill(by_name(name), args.steps, args.warmup)
+        variants[name] = {"ms": r["ms"], "TFLOP/s": r["TFLOP/s"], "GB/s": r["GB/s"],
+                          "mfma_frac": r["roofline"]["frac"], "hbm_frac": r["hbm_frac"]}
+        print(f"# {name}: {r['ms']:.4f} ms", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
+
+    line = {
+        "metric": METRIC, "value": head["TFLOP/s"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1), GPU generator)",
+        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "N": w.Nq, "D": w.D, "mask": w.mask,
+                   "global_batch": w.B, "seq_len": w.Nq, "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "decode": dec,
+        "variants": variants,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

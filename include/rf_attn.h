@@ -1,0 +1,131 @@
+/*
+ * rf_attn.h — C ABI of the MI355X (gfx950) single-pass fused cascaded-reduction
+ * attention library (librfattn.so).
+ *
+ * What is computed.  Attention is "safe softmax followed by a GEMM", the
+ * cascaded reduction named in the abstract of "RedFuser: An Automatic Operator
+ * Fusion Framework for Cascaded Reductions on AI Accelerators" (Tang et al.):
+ *     level 1 (max):       m_i = max_j s_ij
+ *     level 2 (sum):       l_i = sum_j exp(s_ij - m_i)
+ *     level 3 (sum of *):  O_i = sum_j exp(s_ij - m_i) / l_i * v_j
+ * with s_ij = scale * q'_i . k'_j over the keys j visible to query i, fused
+ * into one pass in the incremental form of RedFuser Fig. 4 (each key tile
+ * updates a running (m, l, O) per query row).  q' and k' are q and k after the
+ * optional pre-matmul rotary embedding of "AttnFuse: A Composable DSL for
+ * Compiling Attentions to Fused GPU Kernels" (Dasoju, Zhao; abstract, Fig. 1);
+ * the masks are the causal and sliding-window patterns of AttnFuse Table 6;
+ * split-KV decode with a log-sum-exp merge is RedFuser Fig. 13 / AttnFuse
+ * Table 8.
+ *
+ * Conventions shared by every entry point
+ *  - Layout: q [B, Hq, Nq, D], k and v [B, Hkv, Nk, D], o [B, Hq, Nq, D], all
+ *    contiguous row-major: element (b, h, n, d) is at ((b*H + h)*N + n)*D + d.
+ *    lse [B, Hq, Nq] float32 at (b*Hq + h)*Nq + i.
+ *  - Query row i sits at position Nk - Nq + i, key row j at position j.
+ *    Causal: j visible iff j <= Nk - Nq + i.  Sliding window W: additionally
+ *    j > Nk - Nq + i - W (W counts the diagonal).  A row that sees no key gets
+ *    o = 0 and lse = -inf.
+ *  - GQA: query head h reads KV head h / (Hq / Hkv).
+ *  - RoPE (rope_base > 0): pairs (x[i], x[i + D/2]) of q and k, i < D/2, are
+ *    rotated by angle pos * rope_base^(-2i/D) before the product; v is not
+ *    rotated; rope_base <= 0 disables it.
+ *  - lse is the natural-log log-sum-exp of the scaled, masked, rotated scores.
+ *  - Arithmetic: 16-bit inputs feed MFMA with float32 accumulation; softmax
+ *    state, O accumulation and lse are float32; o is rounded to the input
+ *    dtype once, round-to-nearest-even.
+ *  - Memory: every pointer is device memory owned by the caller; q, k, v, o
+ *    (and o_part) must be 16-byte aligned; outputs must not alias inputs.
+ *    The library never allocates device memory.
+ *  - Asynchrony: each call validates its arguments on the host, enqueues its
+ *    kernels on `stream` (0 = the null stream) and returns; faults during
+ *    execution surface at the caller's next synchronisation.
+ *  - Errors: validation happens before any launch; a non-OK status launches
+ *    nothing.  RF_ERR_INVALID_ARG: null pointer for a non-empty tensor,
+ *    negative size, Hq % Hkv != 0, scale negative or not finite, window < 1
+ *    with the sliding mask, unknown mask or dtype, misaligned pointer.
+ *    RF_ERR_UNSUPPORTED: D not in {64, 128}.  RF_ERR_HIP: a launch failed.
+ *    rf_last_error() returns a thread-local message for the last non-OK
+ *    status of the calling thread.
+ *  - All entry points are thread-safe and keep no state between calls.
+ */
+#ifndef RF_ATTN_H
+#define RF_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RF_OK = 0,
+    RF_ERR_INVALID_ARG = 1,
+    RF_ERR_UNSUPPORTED = 2,
+    RF_ERR_HIP = 3
+} rf_status;
+
+typedef enum { RF_F32 = 0, RF_F16 = 1, RF_BF16 = 2 } rf_dtype;
+
+typedef enum { RF_MASK_NONE = 0, RF_MASK_CAUSAL = 1, RF_MASK_SLIDING = 2 } rf_mask;
+
+/*
+ * rf_attn_fwd — fused forward (RedFuser Fig. 3b / Fig. 4b; AttnFuse Tables 1-7).
+ *
+ * q, k, v: inputs of `dtype` in the layout above.  o: output, same dtype as q.
+ * lse: float32 [B, Hq, Nq], required.  Sizes: B, Nq, Nk >= 0 (zero means an
+ * empty problem: nothing is read; with Nk == 0 every row gets o = 0,
+ * lse = -inf), Hq, Hkv >= 1, D in {64, 128}.  scale >= 0 multiplies q'.k'.
+ * mask_kind: rf_mask.  window: W for RF_MASK_SLIDING, ignored otherwise.
+ * rope_base: > 0 enables RoPE with that base.
+ */
+rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                      float scale, int mask_kind, int window, float rope_base,
+                      int dtype, hipStream_t stream);
+
+/*
+ * rf_attn_splitkv_fwd — split-KV partials (RedFuser Fig. 13, FlashDecoding;
+ * AttnFuse Table 8).  The keys are cut into num_splits chunks; chunk c covers
+ * [c*ceil(Nk/S), min(Nk, (c+1)*ceil(Nk/S))).  For every query row and chunk it
+ * writes the chunk's normalised output and its log-sum-exp:
+ *   o_part   float32 [B, Hq, Nq, S, D]  at (((b*Hq + h)*Nq + i)*S + c)*D + d
+ *   lse_part float32 [B, Hq, Nq, S]     at ((b*Hq + h)*Nq + i)*S + c
+ * A chunk with no visible key gets o_part = 0 and lse_part = -inf.  Other
+ * arguments as rf_attn_fwd.  1 <= num_splits <= 4096.
+ */
+rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v,
+                              float* o_part, float* lse_part,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                              float scale, int mask_kind, int window, float rope_base,
+                              int num_splits, int dtype, hipStream_t stream);
+
+/*
+ * rf_splitkv_workspace_bytes — bytes of o_part plus lse_part for the given
+ * sizes: B*Hq*Nq*num_splits*(D + 1)*4.  Returns 0 for invalid sizes.
+ */
+size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits);
+
+/*
+ * rf_lse_merge — merge split-KV partials by log-sum-exp (the level-1/level-2
+ * cascade applied over chunks, RedFuser Fig. 4 and Fig. 13):
+ *   M = max_c lse_c,  lse = M + ln sum_c exp(lse_c - M),
+ *   o = sum_c exp(lse_c - lse) * o_c, rounded once to out_dtype.
+ * o_part float32 [rows, S, D], lse_part float32 [rows, S]; o [rows, D] of
+ * out_dtype, lse float32 [rows].  Rows whose chunks are all empty get o = 0,
+ * lse = -inf.  rows >= 0, 1 <= num_splits <= 4096, D in {64, 128}.
+ */
+rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                       int rows, int num_splits, int D, int out_dtype, hipStream_t stream);
+
+/* rf_status_string — static text for a status code. */
+const char* rf_status_string(rf_status s);
+
+/* rf_last_error — thread-local detail for the calling thread's last non-OK return. */
+const char* rf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RF_ATTN_H */

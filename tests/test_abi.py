@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+touching any device memory (all pointers here are null or fake)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from attention_pass_cascaded_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rf_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rf_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("librfattn.so is not built; run python -m attention_pass_cascaded_amd.build")
+    return B.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert lib.rf_status_string(code)
+    assert lib.rf_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.rf_splitkv_workspace_bytes(16, 32, 1, 128, 64) == 16 * 32 * 64 * 129 * 4
+    assert lib.rf_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0
+    assert lib.rf_splitkv_workspace_bytes(-1, 1, 1, 64, 1) == 0
+
+
+FAKE = ctypes.c_void_p(4096)   # aligned, never dereferenced: validation fails first
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, D=64,
+             scale=0.125, mask=0, window=0, rope=0.0, dtype=1)
+    a.update(kw)
+    return lib.rf_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                           a["Nq"], a["Nk"], a["D"], a["scale"], a["mask"], a["window"], a["rope"],
+                           a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Hq=3, Hkv=2), B.RF_ERR_INVALID_ARG, "multiple"),
+    (dict(Hkv=0), B.RF_ERR_INVALID_ARG, ">= 1"),
+    (dict(B=-1), B.RF_ERR_INVALID_ARG, "negative"),
+    (dict(Nk=-5), B.RF_ERR_INVALID_ARG, "negative"),
+    (dict(dtype=7), B.RF_ERR_INVALID_ARG, "dtype"),
+    (dict(mask=3), B.RF_ERR_INVALID_ARG, "mask"),
+    (dict(mask=2, window=0), B.RF_ERR_INVALID_ARG, "window"),
+    (dict(scale=-1.0), B.RF_ERR_INVALID_ARG, "scale"),
+    (dict(scale=math.inf), B.RF_ERR_INVALID_ARG, "scale"),
+    (dict(rope=math.nan), B.RF_ERR_INVALID_ARG, "rope"),
+    (dict(D=96), B.RF_ERR_UNSUPPORTED, "96"),
+    (dict(D=256), B.RF_ERR_UNSUPPORTED, "256"),
+    (dict(q=None), B.RF_ERR_INVALID_ARG, "null"),
+    (dict(k=None), B.RF_ERR_INVALID_ARG, "null"),
+    (dict(q=ctypes.c_void_p(4098)), B.RF_ERR_INVALID_ARG, "aligned"),
+    (dict(o=None), B.RF_ERR_INVALID_ARG, "required"),
+    (dict(lse=None), B.RF_ERR_INVALID_ARG, "required"),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status, needle):
+    assert fwd(lib, **kw) == status
+    assert needle in lib.rf_last_error().decode()
+
+
+def test_empty_problem_is_ok_without_touching_memory(lib):
+    assert fwd(lib, q=None, o=None, lse=None, Nq=0) == B.RF_OK
+    assert fwd(lib, q=None, k=None, v=None, o=None, lse=None, B=0) == B.RF_OK
+
+
+def test_splitkv_and_merge_reject_bad_arguments(lib):
+    st = lib.rf_attn_splitkv_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 1, 100, 128, 0.1, 0, 0, 0.0,
+                                 0, 2, None)
+    assert st == B.RF_ERR_INVALID_ARG and b"num_splits" in lib.rf_last_error()
+    st = lib.rf_attn_splitkv_fwd(FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 100, 128, 0.1, 0, 0, 0.0,
+                                 4, 2, None)
+    assert st == B.RF_ERR_INVALID_ARG and b"required" in lib.rf_last_error()
+    assert lib.rf_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 2, None) == B.RF_ERR_INVALID_ARG
+    assert lib.rf_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 8, 80, 2, None) == B.RF_ERR_UNSUPPORTED
+    assert lib.rf_lse_merge(None, FAKE, FAKE, FAKE, 4, 8, 128, 2, None) == B.RF_ERR_INVALID_ARG
+    assert lib.rf_lse_merge(None, None, None, None, 0, 8, 128, 2, None) == B.RF_OK
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    assert fwd(lib, D=96) == B.RF_ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        fwd(lib, Hq=3, Hkv=2)
+        seen["msg"] = lib.rf_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert "multiple" in seen["msg"]
+    assert "96" in lib.rf_last_error().decode()
+
+
+def test_oracle_not_reachable_from_product_package():
+    pkg = os.path.join(ROOT, "attention_pass_cascaded_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

@@ -14,6 +14,7 @@ the window, a wrong GQA head map, a wrong merge weight) fails at least one test:
 """
 import json
 import math
+import zlib
 import os
 
 import numpy as np
@@ -57,7 +58,7 @@ CASES = [
 
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,D,mask,window,base", CASES)
 def test_three_pass_matches_brute_force(B, Hq, Hkv, Nq, Nk, D, mask, window, base):
-    seed = hash((B, Hq, Hkv, Nq, Nk, D, mask, window, base)) % 2**31
+    seed = zlib.crc32(repr((B, Hq, Hkv, Nq, Nk, D, mask, window, base)).encode())
     q, k, v = rnd((B, Hq, Nq, D), seed), rnd((B, Hkv, Nk, D), seed + 1), rnd((B, Hkv, Nk, D), seed + 2)
     scale = 1.0 / math.sqrt(D)
     o, lse = oracle.attention(q, k, v, scale, mask, window, base)

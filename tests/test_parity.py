@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (max-abs over every output element, O and LSE alike): 2e-3 for
+fp16 and fp32, 1e-2 for bf16, as stated for the method's fp16/bf16 outputs
+with fp32 accumulation; fp32 inputs reuse the strictest stated bound.  LSE is
+compared element by element in its [B, Hq, Nq] layout, with the positions of
+-inf (rows that see no key) required to match exactly.  Outputs are poisoned
+with NaN before each launch so an unwritten element fails.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import attention_pass_cascaded_amd as rf
+import oracle
+from workloads import gen_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-3, "f16": 2e-3, "bf16": 1e-2}
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def compare(o, lse, ref_o, ref_lse, tol, what=""):
+    o = o.detach().float().cpu().double().numpy()
+    lse = lse.detach().cpu().double().numpy()
+    assert o.shape == ref_o.shape and lse.shape == ref_lse.shape
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output element"
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(lse), fin), f"{what}: -inf rows differ"
+    assert np.all(lse[~fin] == -np.inf)
+    err_o = float(np.abs(o - ref_o).max()) if o.size else 0.0
+    err_l = float(np.abs(lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+    assert err_o <= tol, f"{what}: max |O - O_ref| = {err_o:.3e} > {tol}"
+    assert err_l <= tol, f"{what}: max |LSE - LSE_ref| = {err_l:.3e} > {tol}"
+    return err_o, err_l
+
+
+def run_fwd(q, k, v, scale, mask, window, rope):
+    dev = torch.device("cuda")
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.full_like(qg, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=dev)
+    o, l = rf.fwd(qg, kg, vg, scale=scale, mask=mask, window=window, rope_base=rope, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o, l
+
+
+FWD_CASES = [
+    # dtype, D, B, Hq, Hkv, Nq, Nk, mask, window, rope
+    ("f16", 64, 1, 2, 2, 129, 129, "none", 0, 0.0),
+    ("f16", 64, 2, 3, 3, 300, 300, "causal", 0, 0.0),
+    ("f16", 64, 1, 4, 2, 70, 300, "causal", 0, 0.0),
+    ("f16", 64, 1, 2, 1, 150, 100, "causal", 0, 0.0),
+    ("f16", 64, 1, 2, 2, 1, 1, "causal", 0, 0.0),
+    ("f16", 64, 1, 2, 2, 17, 17, "none", 0, 0.0),
+    ("f16", 64, 1, 2, 2, 257, 257, "causal", 0, 10000.0),
+    ("f16", 64, 1, 2, 2, 200, 333, "sliding", 37, 10000.0),
+    ("f16", 128, 1, 2, 2, 300, 300, "sliding", 64, 0.0),
+    ("bf16", 128, 1, 2, 2, 520, 520, "sliding", 256, 0.0),
+    ("bf16", 128, 2, 2, 2, 131, 131, "sliding", 1, 0.0),
+    ("bf16", 128, 1, 4, 1, 200, 200, "causal", 0, 10000.0),
+    ("bf16", 64, 1, 2, 2, 190, 190, "none", 0, 500.0),
+    ("bf16", 128, 1, 2, 2, 64, 64, "none", 0, 0.0),
+    ("f32", 64, 1, 1, 1, 256, 256, "none", 0, 0.0),
+    ("f32", 64, 1, 2, 2, 100, 100, "causal", 0, 10000.0),
+    ("f32", 128, 1, 2, 1, 77, 150, "sliding", 40, 0.0),
+]
+
+
+@pytest.mark.parametrize("dt,D,B,Hq,Hkv,Nq,Nk,mask,window,rope", FWD_CASES)
+def test_fwd_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
+    seed = zlib.crc32(repr((dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope)).encode()) % 10_000
+    q, k, v = gen_qkv(B, Hq, Hkv, Nq, Nk, D, dt, seed)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case fwd {dt} D={D} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} {mask} W={window} rope={rope}", flush=True)
+    o, lse = run_fwd(q, k, v, scale, mask, window, rope)
+    ro, rl = oracle.attention(q, k, v, scale, mask, window, rope)
+    compare(o, lse, ro, rl, TOL[dt], "fwd")
+
+
+def test_fwd_empty_keys_gives_zero_and_neg_inf():
+    q, k, v = gen_qkv(1, 2, 2, 40, 0, 64, "f16", 1)
+    o, lse = run_fwd(q, k, v, 0.125, "none", 0, 0.0)
+    assert torch.all(o == 0) and torch.all(lse == -math.inf)
+
+
+def test_fwd_scale_zero_averages_values():
+    q, k, v = gen_qkv(1, 1, 1, 50, 90, 64, "f32", 2)
+    o, lse = run_fwd(q, k, v, 0.0, "causal", 0, 0.0)
+    ro, rl = oracle.attention(q, k, v, 0.0, "causal")
+    compare(o, lse, ro, rl, 1e-5, "scale 0")
+
+
+def test_fwd_is_deterministic():
+    q, k, v = gen_qkv(1, 2, 2, 300, 300, 64, "f16", 3)
+    o1, l1 = run_fwd(q, k, v, 0.125, "causal", 0, 10000.0)
+    o2, l2 = run_fwd(q, k, v, 0.125, "causal", 0, 10000.0)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_runs_on_the_callers_stream():
+    q, k, v = (t.cuda() for t in gen_qkv(1, 2, 2, 256, 256, 64, "f16", 4))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = rf.fwd(q, k, v, scale=0.125, mask="causal")
+    s.synchronize()
+    ro, rl = oracle.attention(q.cpu(), k.cpu(), v.cpu(), 0.125, "causal")
+    compare(o, lse, ro, rl, TOL["f16"], "stream")
+
+
+SPLIT_CASES = [
+    # dtype, D, B, Hq, Hkv, Nq, Nk, S, mask, window, rope     (rows = Hq/Hkv*Nq)
+    ("bf16", 128, 2, 8, 2, 1, 1000, 7, "none", 0, 0.0),       # decode kernel, 4 rows
+    ("bf16", 128, 1, 4, 4, 1, 512, 1, "none", 0, 0.0),        # 1 row, 1 chunk
+    ("f16", 64, 1, 8, 1, 1, 700, 64, "none", 0, 0.0),         # 8 rows, chunks of 11
+    ("f16", 64, 1, 4, 2, 3, 300, 5, "causal", 0, 0.0),        # 6 rows, causal with Nq < Nk
+    ("bf16", 128, 1, 4, 1, 2, 400, 3, "sliding", 100, 10000.0),
+    ("f32", 128, 1, 2, 2, 1, 333, 4, "none", 0, 10000.0),
+    ("f16", 128, 1, 2, 2, 1, 50, 64, "none", 0, 0.0),         # more chunks than keys/chunk
+    ("f16", 64, 1, 2, 2, 40, 300, 3, "causal", 0, 0.0),       # 40 rows: MFMA split path
+    ("bf16", 128, 1, 4, 2, 100, 100, 4, "sliding", 30, 10000.0),
+]
+
+
+@pytest.mark.parametrize("dt,D,B,Hq,Hkv,Nq,Nk,S,mask,window,rope", SPLIT_CASES)
+def test_splitkv_and_merge_match_oracle(dt, D, B, Hq, Hkv, Nq, Nk, S, mask, window, rope):
+    seed = zlib.crc32(repr((dt, D, B, Hq, Hkv, Nq, Nk, S, mask, window, rope)).encode()) % 10_000
+    q, k, v = gen_qkv(B, Hq, Hkv, Nq, Nk, D, dt, seed)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case split {dt} D={D} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} S={S} {mask} W={window} rope={rope}", flush=True)
+    dev = torch.device("cuda")
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    op = torch.full((B, Hq, Nq, S, D), float("nan"), device=dev)
+    lp = torch.full((B, Hq, Nq, S), float("nan"), device=dev)
+    rf.splitkv_fwd(qg, kg, vg, S, scale, mask, window, rope, o_part=op, lse_part=lp)
+    o, lse = rf.lse_merge(op, lp, out_dtype=DT[dt])
+    torch.cuda.synchronize()
+    rop, rlp = oracle.split_partials(q, k, v, scale, S, mask, window, rope)
+    compare(op, lp, rop, rlp, TOL[dt], "partials (fp32)")
+    ro, rl = oracle.attention(q, k, v, scale, mask, window, rope)
+    compare(o, lse, ro, rl, TOL[dt], "merged")
+
+
+def test_merge_matches_oracle_with_empty_chunks():
+    g = torch.Generator().manual_seed(11)
+    op = torch.randn((3, 5, 9, 128), generator=g)
+    lp = torch.randn((3, 5, 9), generator=g) * 4
+    lp[0, 1, 2] = -math.inf
+    lp[2, 3, :] = -math.inf            # a row with every chunk empty
+    op[2, 3] = 0.0
+    o, lse = rf.lse_merge(op.cuda(), lp.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_merge(op, lp)
+    compare(o, lse, ro, rl, 1e-5, "merge")

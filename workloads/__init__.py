@@ -5,10 +5,13 @@ none of the attention arithmetic: no scores, no softmax, no rotation, no merge.
 Both the fp64 oracle and the HIP kernels consume exactly the tensors produced
 here, so that input quantisation is never counted as kernel error.
 
-Recipe (one CPU generator per workload, seed fixed in advance):
+Recipe (one generator per workload, seed fixed in advance):
   q, then k, then v are drawn in that order as float32 N(0, 1) from
-  ``torch.Generator().manual_seed(seed)`` and cast with round-to-nearest-even
-  to the workload's dtype.  Layout is contiguous [B, H, N, D] row-major.
+  ``torch.Generator(device).manual_seed(seed)`` and cast with
+  round-to-nearest-even to the workload's dtype.  Layout is contiguous
+  [B, H, N, D] row-major.  Small cases draw on the CPU; full-size workloads
+  draw on the GPU (the 2 x 537M-element decode cache takes ~40 s on the CPU),
+  and the oracle is then handed exact copies of the slices it needs.
 
 The shapes follow the workloads the pages measure on: the AttnFuse listing's
 causal forward at B=4 H=12 N=4096 D=64 fp16 (its Tables 1-3), its RoPE+causal
@@ -79,25 +82,26 @@ def by_name(name: str) -> Workload:
 
 def gen_normal(shape, dtype: torch.dtype, gen: torch.Generator) -> torch.Tensor:
     """float32 N(0,1) draw, then a round-to-nearest-even cast to ``dtype``."""
-    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=gen.device)
     return x.to(dtype) if dtype != torch.float32 else x
 
 
-def gen_qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed):
-    """Draw (q, k, v) on the CPU in the fixed order q, k, v.
+def gen_qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed, device="cpu"):
+    """Draw (q, k, v) in the fixed order q, k, v with a generator on ``device``.
 
     ``dtype`` is a torch dtype or one of "f32", "f16", "bf16".
-    Returns contiguous CPU tensors of shapes [B,Hq,Nq,D], [B,Hkv,Nk,D], [B,Hkv,Nk,D].
+    Returns contiguous tensors of shapes [B,Hq,Nq,D], [B,Hkv,Nk,D], [B,Hkv,Nk,D].
     """
     if isinstance(dtype, str):
         dtype = _DT[dtype]
-    g = torch.Generator().manual_seed(int(seed))
+    g = torch.Generator(device=device).manual_seed(int(seed))
     q = gen_normal((B, Hq, Nq, D), dtype, g)
     k = gen_normal((B, Hkv, Nk, D), dtype, g)
     v = gen_normal((B, Hkv, Nk, D), dtype, g)
     return q, k, v
 
 
-def gen_workload(w: Workload, seed: int | None = None):
+def gen_workload(w: Workload, seed: int | None = None, device="cpu"):
     return gen_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, w.torch_dtype,
-                   w.seed if seed is None else seed)
+                   w.seed if seed is None else seed, device=device)
+
