@@ -72,6 +72,20 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// acc + sum of 8 packed 16-bit values, float32 accumulation (v_dot2 with ones).
+__device__ __forceinline__ float row_sum8(const f16x8& v, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) acc = __builtin_amdgcn_fdot2(f16x2{v[i], v[i + 1]}, one, acc, false);
+    return acc;
+}
+__device__ __forceinline__ float row_sum8(const bf16x8& v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[i], v[i + 1]}, one, acc, false);
+    return acc;
+}
+
 // Exchange with the lane 32 away (the other half of the wavefront).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -15,12 +15,17 @@
 //   registers), so lane l owns query row (l % 32) and 16 keys per 32-key
 //   block: the row max and row sum are in-lane plus one swap between the two
 //   32-lane halves.
-//   O^T += V^T . P^T on MFMA 32x32 (A = V^T from LDS, B = P^T straight from
-//   the score registers), so the rescale of O by alpha is a per-lane scalar.
-// K is staged row-major in LDS; V is written transposed (d-major) with the key
-// slots permuted so each lane's 8 contraction slots are 16 contiguous bytes.
+//   O^T += V^T . P^T on MFMA 32x32 (A = V^T, B = P^T straight from the score
+//   registers), so the rescale of O by alpha is a per-lane scalar.  V stays
+//   row-major in LDS; the transposed operand comes from the gfx950 LDS
+//   transpose read (ds_read_b64_tr_b16), 4 keys of one d column per lane.
 // K/V tiles are double-buffered: the global loads of tile t+1 are issued
 // before the math of tile t and written to LDS after it (one barrier a tile).
+//
+// The O rescale is lazy: the reference max m_ref only moves when a tile's max
+// exceeds it by more than 2^8, so P = 2^(s - m_ref) <= 256 (exact range in
+// fp16 and bf16) and l, O stay consistent with m_ref; the final O / l is the
+// same quantity.
 #pragma once
 
 #include "common.hpp"
@@ -37,23 +42,21 @@ struct FwdCfg {
     static constexpr int BN = F32 ? 32 : 64;            // keys per tile
     static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
     static constexpr int CPR = D / EPC;                 // chunks per row
-    static constexpr int KSTRIDE = D + EPC;             // K row pitch (elements), +16 B
-    static constexpr int VROWS = F32 ? BN : D;          // f32 keeps V row-major
-    static constexpr int VSTRIDE = F32 ? D + EPC : BN + 8;
+    static constexpr int KSTRIDE = D + EPC;             // row pitch (elements), +16 B
     static constexpr int K_ELEMS = BN * KSTRIDE * (SPLITK ? 2 : 1);  // hi tile, then lo tile
-    static constexpr int STAGE = K_ELEMS + VROWS * VSTRIDE;
+    static constexpr int STAGE = K_ELEMS + BN * KSTRIDE;  // + V tile, row-major
     static constexpr int CH = BN * CPR / FWD_THREADS;   // 16-byte chunks per thread per tile
-    static constexpr int RPW = 64 / CPR;                // key rows one wave covers per chunk
     static_assert(CH >= 2 && CH % 2 == 0, "tile must give each thread an even chunk count");
 };
 
-// Key slot inside a 16-bit V^T tile: bits 2 and 3 of the key index swapped.
-// MFMA output register j of lane-half h holds key 8*(j/4) + 4*h + j%4 of its
-// 32-key block; feeding registers 8t..8t+7 as one B operand makes contraction
-// slot (h, i) key 16t + 8*(i/4) + 4*h + i%4, which this swap stores at
-// 16t + 8*h + i.
-__device__ __forceinline__ int vt_slot(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS transpose read: in each 16-lane group, lane j names 4 consecutive
+// 16-bit elements M[j][0..3]; lane i receives M[4k + i/4][i%4] in slot k.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ptr));
 }
 
 template <typename T, int D, bool ROPE>
@@ -64,10 +67,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
     constexpr int BN = C::BN;
     constexpr int EPC = C::EPC;
     constexpr int CPR = C::CPR;
+    constexpr int KS = C::KSTRIDE;
     constexpr int NKB = BN / 32;      // 32-key blocks per tile
     constexpr int NDB = D / 32;       // 32-wide d blocks of the output
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr float LN2 = 0.6931471805599453f;
+    constexpr float RESCALE_SLACK = 8.0f;  // log2 units
     typedef typename Vec16<T>::type VecT;
 
     __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
@@ -104,8 +109,13 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
     const int pw_max = min(p.Nq, wrow0 + 32) - 1 + pos_off;
     const int my_row = wrow0 + l32;
     const int my_pos = my_row + pos_off;
+    // visible keys of this lane's row: lim_lo <= key <= lim_hi
+    const int lim_hi = p.mask != RF_MASK_NONE ? min(khi - 1, my_pos) : khi - 1;
+    const int lim_lo = p.mask == RF_MASK_SLIDING ? my_pos - p.window + 1 : -(1 << 30);
 
-    const float c = p.scale * LOG2E;
+    // log2-domain scale; kept >= 1e-30 so masked -inf scores stay -inf after
+    // the multiply (scale 0 then gives exactly uniform weights).
+    const float c = fmaxf(p.scale * LOG2E, 1e-30f);
     const size_t kv_base = ((size_t)b * p.Hkv + g) * (size_t)p.Nk * D;
     const T* __restrict__ kg = (const T*)p.k + kv_base;
     const T* __restrict__ vg = (const T*)p.v + kv_base;
@@ -117,12 +127,18 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
     constexpr int QN = D / 2;
     float qf[QN];
     {
-        const T* qrow = (const T*)p.q + (((size_t)b * p.Hq + h) * p.Nq + (size_t)my_row) * D;
         const bool ok = my_row < p.Nq;
+        const T* qrow = (const T*)p.q + (((size_t)b * p.Hq + h) * p.Nq + (size_t)min(my_row, p.Nq - 1)) * D;
+        if constexpr (F32) {
 #pragma unroll
-        for (int n = 0; n < QN; ++n) {
-            const int d = F32 ? 2 * n + hi : 16 * (n / 8) + 8 * hi + (n % 8);
-            qf[n] = ok ? to_f32(qrow[d]) : 0.f;
+            for (int n = 0; n < QN; ++n) qf[n] = ok ? qrow[2 * n + hi] : 0.f;
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const VecT x = *(const VecT*)(qrow + 16 * ks + 8 * hi);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qf[8 * ks + i] = ok ? to_f32(x[i]) : 0.f;
+            }
         }
         if (ROPE) {
 #pragma unroll
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
         for (int e = 0; e < EPC; ++e) ipd[e] = rope_inv_period(p.rope_base, cc * EPC + e, D);
     }
 
-    // ---------------- tile staging
+    // ---------------- tile staging (global -> registers -> LDS)
     uint4 kreg[C::CH], vreg[C::CH];
 
     auto load_tile = [&](int k0) {
@@ -183,18 +199,9 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
-            int row, ch;
-            if (F32) {
-                const int u = it * FWD_THREADS + tid;
-                row = u / CPR;
-                ch = u % CPR;
-            } else {
-                const int slot = C::RPW * (it * FWD_WAVES + wave) + lane / CPR;
-                row = vt_slot(slot);
-                ch = lane % CPR;
-            }
-            const int key = k0 + row;
-            vreg[it] = key < p.Nk ? *(const uint4*)(vg + (size_t)key * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+            const int u = it * FWD_THREADS + tid;
+            const int key = k0 + u / CPR;
+            vreg[it] = key < p.Nk ? *(const uint4*)(vg + (size_t)key * D + (u % CPR) * EPC) : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -208,8 +215,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
                 const int row = u / (CPR / 2);
                 const int cc = u % (CPR / 2);
                 const int pos = k0 + row;
-                VecT lo = *(VecT*)&kreg[it];
-                VecT hi_ = *(VecT*)&kreg[it + 1];
+                const VecT lo = *(const VecT*)&kreg[it];
+                const VecT hi_ = *(const VecT*)&kreg[it + 1];
                 VecT olo, ohi, rlo, rhi;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
@@ -224,44 +231,41 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
                         rhi[e] = from_f32<T>(yr - to_f32(ohi[e]));
                     }
                 }
-                *(VecT*)(ks_ + row * C::KSTRIDE + cc * EPC) = olo;
-                *(VecT*)(ks_ + row * C::KSTRIDE + (cc + CPR / 2) * EPC) = ohi;
+                *(VecT*)(ks_ + row * KS + cc * EPC) = olo;
+                *(VecT*)(ks_ + row * KS + (cc + CPR / 2) * EPC) = ohi;
                 if constexpr (SPLITK) {
-                    T* kl = ks_ + BN * C::KSTRIDE;
-                    *(VecT*)(kl + row * C::KSTRIDE + cc * EPC) = rlo;
-                    *(VecT*)(kl + row * C::KSTRIDE + (cc + CPR / 2) * EPC) = rhi;
+                    T* kl = ks_ + BN * KS;
+                    *(VecT*)(kl + row * KS + cc * EPC) = rlo;
+                    *(VecT*)(kl + row * KS + (cc + CPR / 2) * EPC) = rhi;
                 }
             }
         } else {
 #pragma unroll
             for (int it = 0; it < C::CH; ++it) {
                 const int u = it * FWD_THREADS + tid;
-                *(uint4*)(ks_ + (u / CPR) * C::KSTRIDE + (u % CPR) * EPC) = kreg[it];
+                *(uint4*)(ks_ + (u / CPR) * KS + (u % CPR) * EPC) = kreg[it];
             }
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
-            if constexpr (F32) {
-                const int u = it * FWD_THREADS + tid;
-                *(uint4*)(vs_ + (u / CPR) * C::VSTRIDE + (u % CPR) * EPC) = vreg[it];
-            } else {
-                const int slot = C::RPW * (it * FWD_WAVES + wave) + lane / CPR;
-                const int ch = lane % CPR;
-                VecT x = *(VecT*)&vreg[it];
-#pragma unroll
-                for (int e0 = 0; e0 < 8; ++e0) {
-                    const int e = (e0 + ch) & 7;  // stagger: lanes of one row hit different banks
-                    vs_[(ch * 8 + e) * C::VSTRIDE + slot] = x[e];
-                }
-            }
+            const int u = it * FWD_THREADS + tid;
+            *(uint4*)(vs_ + (u / CPR) * KS + (u % CPR) * EPC) = vreg[it];
         }
     };
+
+    // V^T operand addressing for the transpose read (16-bit types): lane
+    // (q = lane/16, j = lane%16) names V[16t + 4*hi + j/4 (+8)][32db + 16(q&1) + 4(j&3)]
+    // and receives V[16t + 4*hi + k (+8)][32db + lane%32] in slot k = 0..3, so
+    // contraction slot (hi, i) holds key 16t + 8*(i/4) + 4*hi + i%4: the key of
+    // score register 8*(t%2) + i in this lane half.
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // ---------------- running state
     f32x16 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;
+    float m_ref = -INFINITY;  // reference max (log2 units of the scaled scores)
     float l_run = 0.f;
 
     if (ntiles > 0) {
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 sacc[kb] = f32x16{};
-                const T* krow = ks_ + (32 * kb + l32) * C::KSTRIDE;
+                const T* krow = ks_ + (32 * kb + l32) * KS;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     if constexpr (F32) {
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
                         const VecT a = *(const VecT*)(krow + 16 * ks + 8 * hi);
                         sacc[kb] = mfma32(a, qv[ks], sacc[kb]);
                         if constexpr (SPLITK) {
-                            const VecT al = *(const VecT*)(krow + BN * C::KSTRIDE + 16 * ks + 8 * hi);
+                            const VecT al = *(const VecT*)(krow + BN * KS + 16 * ks + 8 * hi);
                             sacc[kb] = mfma32(a, qlo[ks], sacc[kb]);
                             sacc[kb] = mfma32(al, qv[ks], sacc[kb]);
                         }
@@ -314,57 +318,57 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
             }
 
             if (need_mask) {
+                // register j of block kb holds key k0 + 4*hi + 32*kb + 8*(j/4) + j%4
+                const int rel_hi = lim_hi - k0 - 4 * hi;
+                const int rel_lo = lim_lo - k0 - 4 * hi;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const int key = k0 + 32 * kb + 8 * (j / 4) + 4 * hi + (j % 4);
-                        bool vis = key < khi;
-                        if (p.mask != RF_MASK_NONE) vis &= key <= my_pos;
-                        if (p.mask == RF_MASK_SLIDING) vis &= key > my_pos - p.window;
-                        if (!vis) sacc[kb][j] = -INFINITY;
+                        const int off = 32 * kb + 8 * (j / 4) + (j % 4);
+                        sacc[kb][j] = (off <= rel_hi && off >= rel_lo) ? sacc[kb][j] : -INFINITY;
                     }
             }
 
-            // level 1: running max (log2 domain of the scaled scores)
+            // level 1: tile max (log2 domain of the scaled scores)
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
             mx = fmaxf(mx, swap_halves(mx));
-            const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
-            const float m_new = fmaxf(m_run, m_tile);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
+            const float m_tile = mx * c;
 
-            // level 2 and the correction of level 3
-            l_run *= alpha;
+            // lazy correction of levels 2 and 3: only when the max moved by > 2^8
+            const bool bump = m_tile > m_ref + RESCALE_SLACK;
+            if (__builtin_amdgcn_ballot_w64(bump)) {
+                const float m_new = bump ? m_tile : m_ref;
+                const float alpha = bump ? fast_exp2(m_ref - m_new) : 1.f;  // m_ref = -inf -> 0
+                m_ref = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            }
+            const float m_sub = (m_ref == -INFINITY) ? 0.f : m_ref;
 
+            // level 2 terms: P = 2^(s*c - m_ref); masked entries give 2^-inf = 0
             float pr[NKB][16];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    float e = fast_exp2(fmaf(sacc[kb][j], c, -m_use));
-                    if (need_mask) e = (sacc[kb][j] == -INFINITY) ? 0.f : e;
-                    pr[kb][j] = e;
-                    l_run += e;
-                }
+                for (int j = 0; j < 16; ++j) pr[kb][j] = fast_exp2(fmaf(sacc[kb][j], c, -m_sub));
 
-            // level 3: O^T += V^T . P^T
+            // level 3: O^T += V^T . P^T (16-bit: the rounded P also feeds l)
             if constexpr (F32) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
+                        l_run += pr[kb][j];
                         const int key = 32 * kb + 8 * (j / 4) + 4 * hi + (j % 4);
 #pragma unroll
                         for (int db = 0; db < NDB; ++db)
-                            oacc[db] = mfma32(vs_[key * C::VSTRIDE + 32 * db + l32], pr[kb][j], oacc[db]);
+                            oacc[db] = mfma32(vs_[key * KS + 32 * db + l32], pr[kb][j], oacc[db]);
                     }
             } else {
 #pragma unroll
@@ -372,10 +376,14 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
                     VecT pb;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) pb[i] = from_f32<T>(pr[t16 / 2][8 * (t16 % 2) + i]);
+                    l_run = row_sum8(pb, l_run);
+                    const T* vrow = vs_ + (16 * t16 + tr_row) * KS + tr_col;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const VecT a = *(const VecT*)(vs_ + (32 * db + l32) * C::VSTRIDE + 16 * t16 + 8 * hi);
-                        oacc[db] = mfma32(a, pb, oacc[db]);
+                        const i16x4 lo4 = lds_read_tr16(vrow + 32 * db);
+                        const i16x4 hi4 = lds_read_tr16(vrow + 8 * KS + 32 * db);
+                        const i16x8 ab = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[db] = mfma32(__builtin_bit_cast(VecT, ab), pb, oacc[db]);
                     }
                 }
             }
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
     const float l_tot = l_run + swap_halves(l_run);
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
-    const float lse_v = live ? (m_run + fast_log2(l_tot)) * LN2 : -INFINITY;
+    const float lse_v = live ? (m_ref + fast_log2(l_tot)) * LN2 : -INFINITY;
     if (!wave_live || my_row >= p.Nq) return;
     const size_t row_id = ((size_t)b * p.Hq + h) * p.Nq + (size_t)my_row;
     if (p.split_mode) {
@@ -398,20 +406,22 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * db + 8 * jq + 4 * hi;
-                float4 w = make_float4(oacc[db][4 * jq] * inv, oacc[db][4 * jq + 1] * inv,
-                                       oacc[db][4 * jq + 2] * inv, oacc[db][4 * jq + 3] * inv);
-                *(float4*)(orow + d0) = w;
+                *(float4*)(orow + d0) = make_float4(oacc[db][4 * jq] * inv, oacc[db][4 * jq + 1] * inv,
+                                                    oacc[db][4 * jq + 2] * inv, oacc[db][4 * jq + 3] * inv);
             }
         if (hi == 0) p.lse_part[row_id * p.num_splits + split] = lse_v;
     } else {
         T* orow = (T*)p.o + row_id * D;
+        typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * db + 8 * jq + 4 * hi;
+                T4 w;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) orow[d0 + r] = from_f32<T>(oacc[db][4 * jq + r] * inv);
+                for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(oacc[db][4 * jq + r] * inv);
+                *(T4*)(orow + d0) = w;
             }
         if (hi == 0) p.lse[row_id] = lse_v;
     }
