@@ -128,7 +128,8 @@ rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float
     p.split_len = (Nk + num_splits - 1) / num_splits;
     p.split_mode = 1;
     const int rows = (Hq / Hkv) * Nq;
-    if (rows <= rf::DEC_MAX_ROWS && Hkv <= 65535 && B <= 65535)
+    const int max_rows = dtype == RF_F32 ? rf::DEC_MAX_ROWS_F32 : rf::DEC_MAX_ROWS_16;
+    if (rows <= max_rows && Hkv <= 65535 && B <= 65535)
         return hip_status(launch_decode(p, dtype, stream), "rf_attn_splitkv_fwd decode launch");
     if ((Nq + rf::FWD_BM - 1) / rf::FWD_BM > 65535) return fail(RF_ERR_INVALID_ARG, "Nq too large");
     if ((size_t)B * Hq * num_splits > 0x7fffffffu) return fail(RF_ERR_INVALID_ARG, "B*Hq*num_splits too large");

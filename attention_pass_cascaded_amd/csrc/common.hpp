@@ -72,6 +72,16 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS transpose read: in each 16-lane group, lane j names 4 consecutive
+// 16-bit elements M[j][0..3]; lane i receives M[4k + i/4][i%4] in slot k.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ptr));
+}
+
 // acc + sum of 8 packed 16-bit values, float32 accumulation (v_dot2 with ones).
 __device__ __forceinline__ float row_sum8(const f16x8& v, float acc) {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};

@@ -49,16 +49,6 @@ struct FwdCfg {
     static_assert(CH >= 2 && CH % 2 == 0, "tile must give each thread an even chunk count");
 };
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// LDS transpose read: in each 16-lane group, lane j names 4 consecutive
-// 16-bit elements M[j][0..3]; lane i receives M[4k + i/4][i%4] in slot k.
-__device__ __forceinline__ i16x4 lds_read_tr16(const void* ptr) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ptr));
-}
-
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);

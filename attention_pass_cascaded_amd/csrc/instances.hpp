@@ -2,6 +2,7 @@
 #pragma once
 
 #include "decode_kernel.hpp"
+#include "decode_mfma_kernel.hpp"
 #include "fwd_kernel.hpp"
 #include "launch.hpp"
 
@@ -39,9 +40,24 @@ hipError_t dec_launch_d(const AttnParams& p, hipStream_t s) {
     return dec_launch_rows<T, D, 8>(p, s);
 }
 
+template <typename T, int D>
+hipError_t dec_mfma_launch_d(const AttnParams& p, hipStream_t s) {
+    dim3 grid((unsigned)p.num_splits, (unsigned)p.Hkv, (unsigned)p.B);
+    if (p.rope_base > 0.f)
+        hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, true>), grid, dim3(DM_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, false>), grid, dim3(DM_THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+// 16-bit inputs: matrix-core streaming kernel (<= 16 rows per KV head);
+// float32 inputs: vector-ALU streaming kernel (<= 8 rows per KV head).
 template <typename T>
 hipError_t dec_dispatch(const AttnParams& p, hipStream_t s) {
-    return p.D == 64 ? dec_launch_d<T, 64>(p, s) : dec_launch_d<T, 128>(p, s);
+    if constexpr (sizeof(T) == 2)
+        return p.D == 64 ? dec_mfma_launch_d<T, 64>(p, s) : dec_mfma_launch_d<T, 128>(p, s);
+    else
+        return p.D == 64 ? dec_launch_d<T, 64>(p, s) : dec_launch_d<T, 128>(p, s);
 }
 
 }  // namespace rf

@@ -10,8 +10,10 @@ hipError_t launch_fwd_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_fwd_f16(const AttnParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(const AttnParams& p, hipStream_t s);
 
-// Split-KV partials on the streaming decode kernel; needs (Hq/Hkv)*Nq <= DEC_MAX_ROWS.
-constexpr int DEC_MAX_ROWS = 8;
+// Split-KV partials on the streaming decode kernels; they serve all
+// (Hq/Hkv)*Nq query rows of a KV head at once, up to this many.
+constexpr int DEC_MAX_ROWS_F32 = 8;
+constexpr int DEC_MAX_ROWS_16 = 16;
 hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_decode_f16(const AttnParams& p, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);

@@ -123,6 +123,13 @@ SPLIT_CASES = [
     ("f16", 128, 1, 2, 2, 1, 50, 64, "none", 0, 0.0),         # more chunks than keys/chunk
     ("f16", 64, 1, 2, 2, 40, 300, 3, "causal", 0, 0.0),       # 40 rows: MFMA split path
     ("bf16", 128, 1, 4, 2, 100, 100, 4, "sliding", 30, 10000.0),
+    ("bf16", 128, 1, 16, 1, 1, 900, 5, "none", 0, 0.0),       # 16 rows: widest decode group
+    ("f16", 64, 2, 8, 2, 4, 777, 6, "causal", 0, 0.0),        # 16 rows, causal, Nq < Nk
+    ("f16", 128, 1, 8, 8, 1, 300, 2, "sliding", 50, 10000.0), # 1 row, f16 RoPE
+    ("bf16", 64, 1, 12, 4, 2, 260, 3, "causal", 0, 10000.0),  # 6 rows, bf16 RoPE (hi/lo split)
+    ("f32", 64, 1, 8, 1, 1, 200, 3, "none", 0, 0.0),          # float32: vector-ALU decode, 8 rows
+    ("f32", 128, 1, 9, 1, 1, 200, 3, "none", 0, 0.0),         # float32, 9 rows: MFMA split path
+    ("bf16", 128, 1, 17, 1, 1, 300, 2, "none", 0, 0.0),       # 17 rows: MFMA split path
 ]
 
 
