@@ -30,15 +30,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def flags():
+def flags(extra=()):
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
+            "-I", os.path.join(ROOT, "include"), "-Wno-unused-result", *extra]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(src: str, verbose: bool, obj_dir: str, extra=()) -> str:
+    out = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *flags(extra), "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,20 +51,27 @@ def _compile(src: str, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, extra_flags=(), out: str | None = None) -> str:
+    """Compile every source and link the library.
+
+    ``extra_flags`` (e.g. -D tuning macros) and ``out`` (another library path)
+    let a tile or schedule setting be built beside the default one.
+    """
+    lib = out or LIB
+    obj_dir = OBJ if out is None else os.path.join(OBJ, os.path.basename(out).replace(".so", ""))
+    os.makedirs(obj_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, obj_dir, tuple(extra_flags)), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

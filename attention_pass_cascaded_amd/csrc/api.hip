@@ -52,6 +52,8 @@ rf_status check_attn(const void* q, const void* k, const void* v, int B, int Hq,
     if ((q && !aligned16(q)) || (k && !aligned16(k)) || (v && !aligned16(v)))
         return fail(RF_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
     if ((size_t)B * Hq > (size_t)1 << 30) return fail(RF_ERR_INVALID_ARG, "B*Hq too large");
+    if ((size_t)Nk * D * (dtype == RF_F32 ? 4 : 2) >= ((size_t)1 << 31))
+        return fail(RF_ERR_UNSUPPORTED, "one KV head must be < 2 GiB (Nk*D*elem_size)");
     p = rf::AttnParams{};
     p.q = q;
     p.k = k;
@@ -145,8 +147,9 @@ rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, floa
     if (D != 64 && D != 128) return fail(RF_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
     if (rows == 0) return RF_OK;
     if (!o_part || !lse_part || !o || !lse) return fail(RF_ERR_INVALID_ARG, "null pointer");
-    if (((uintptr_t)o_part & 3u) || ((uintptr_t)lse_part & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)o & 3u))
-        return fail(RF_ERR_INVALID_ARG, "misaligned pointer");
+    if (((uintptr_t)o_part & 15u) || ((uintptr_t)lse_part & 3u) || ((uintptr_t)lse & 3u) ||
+        ((uintptr_t)o & (out_dtype == RF_F32 ? 15u : 7u)))
+        return fail(RF_ERR_INVALID_ARG, "misaligned pointer (o_part 16 B, o 4 elements, lse 4 B)");
     return hip_status(rf::launch_merge(o_part, lse_part, o, lse, rows, num_splits, D, out_dtype, stream),
                       "rf_lse_merge launch");
 }
@@ -169,7 +172,7 @@ namespace rf {
 
 template <typename T, int D>
 static hipError_t merge_one(const float* op, const float* lp, void* o, float* lse, int rows, int S, hipStream_t s) {
-    dim3 grid((unsigned)((rows + MRG_ROWS - 1) / MRG_ROWS));
+    dim3 grid((unsigned)rows);
     hipLaunchKernelGGL((lse_merge_kernel<T, D>), grid, dim3(MRG_THREADS), 0, s, op, lp, (T*)o, lse, rows, S);
     return hipGetLastError();
 }

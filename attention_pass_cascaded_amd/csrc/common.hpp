@@ -96,8 +96,25 @@ __device__ __forceinline__ float row_sum8(const bf16x8& v, float acc) {
     return acc;
 }
 
-// Exchange with the lane 32 away (the other half of the wavefront).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Exchange with the lane 32 away (the other half of the wavefront):
+// v_permlane32_swap trades the upper half of its first operand with the lower
+// half of its second, so with x in both, lanes 0-31 find x[l+32] in the second
+// result and lanes 32-63 find x[l-32] in the first.
+__device__ __forceinline__ float swap_halves(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+}
+
+// Raw buffer resource over [base, base + bytes): 16-byte loads at byte
+// offsets at or past `bytes` return zeros without touching memory.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
 
 // RoPE angle of frequency i at integer position pos, returned as (cos, sin).
 // inv_period = theta_i / (2*pi) is kept in double so the product with large

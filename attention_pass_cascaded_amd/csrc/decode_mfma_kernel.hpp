@@ -77,8 +77,11 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
 
     const float c = fmaxf(p.scale * LOG2E, 1e-30f);
     const size_t kv_base = ((size_t)b * p.Hkv + g) * (size_t)p.Nk * D;
-    const T* __restrict__ kg = (const T*)p.k + kv_base;
-    const T* __restrict__ vg = (const T*)p.v + kv_base;
+    // K and V of this (batch, KV head); rows past Nk read as zeros.  Rows in
+    // [khi, Nk) belong to the next chunk: they are loaded but masked out.
+    const int kv_bytes = p.Nk * D * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)p.k + kv_base, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)p.v + kv_base, kv_bytes);
 
     // ---- this lane's query row: head g*G + n/Nq, query n%Nq
     const bool row_ok = n < rows;
@@ -145,14 +148,13 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
             const int key = k0 + 16 * kgp + n;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                ka[kgp][ks] = key < khi ? *(const VecT*)(kg + (size_t)key * D + 32 * ks + 8 * q) : VecT{};
+                ka[kgp][ks] = __builtin_bit_cast(VecT, buf_load16(krs, (key * D + 32 * ks + 8 * q) * (int)sizeof(T)));
         }
         uint4 vr[VLD];
 #pragma unroll
         for (int it = 0; it < VLD; ++it) {
             const int u = it * 64 + lane;
-            const int key = k0 + u / CPR;
-            vr[it] = key < khi ? *(const uint4*)(vg + (size_t)key * D + (u % CPR) * 8) : make_uint4(0, 0, 0, 0);
+            vr[it] = buf_load16(vrs, ((k0 + u / CPR) * D + (u % CPR) * 8) * (int)sizeof(T));
         }
 
         // ---- RoPE on K (pairs are in-lane: ks and ks + NKS/2)

@@ -49,8 +49,15 @@ struct FwdCfg {
     static_assert(CH >= 2 && CH % 2 == 0, "tile must give each thread an even chunk count");
 };
 
+// Waves per SIMD the non-RoPE D=64 instance is compiled for (register budget
+// 512 / waves); 4 measured best for the causal fp16 workload (LDS allows 4
+// work-groups per CU).  The other instances need more registers and get 2.
+#ifndef RF_FWD_WAVES_D64
+#define RF_FWD_WAVES_D64 4
+#endif
+
 template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
     using C = FwdCfg<T, D, SPLITK>;
     constexpr bool F32 = C::F32;
@@ -107,8 +114,10 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
     // the multiply (scale 0 then gives exactly uniform weights).
     const float c = fmaxf(p.scale * LOG2E, 1e-30f);
     const size_t kv_base = ((size_t)b * p.Hkv + g) * (size_t)p.Nk * D;
-    const T* __restrict__ kg = (const T*)p.k + kv_base;
-    const T* __restrict__ vg = (const T*)p.v + kv_base;
+    // K and V of this (batch, KV head); rows past Nk read as zeros
+    const int kv_bytes = p.Nk * D * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)p.k + kv_base, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)p.v + kv_base, kv_bytes);
 
     // ---------------- Q^T operand (+ RoPE), loaded once
     // lane element n in [0, D/2): d(n) = 16*(n/8) + 8*hi + n%8 (16-bit)
@@ -184,14 +193,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
                 row = u / CPR;
                 ch = u % CPR;
             }
-            const int key = k0 + row;
-            kreg[it] = key < p.Nk ? *(const uint4*)(kg + (size_t)key * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+            kreg[it] = buf_load16(krs, ((k0 + row) * D + ch * EPC) * (int)sizeof(T));
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
             const int u = it * FWD_THREADS + tid;
-            const int key = k0 + u / CPR;
-            vreg[it] = key < p.Nk ? *(const uint4*)(vg + (size_t)key * D + (u % CPR) * EPC) : make_uint4(0, 0, 0, 0);
+            vreg[it] = buf_load16(vrs, ((k0 + u / CPR) * D + (u % CPR) * EPC) * (int)sizeof(T));
         }
     };
 
@@ -316,7 +323,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_kernel(AttnParams p) 
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int off = 32 * kb + 8 * (j / 4) + (j % 4);
-                        sacc[kb][j] = (off <= rel_hi && off >= rel_lo) ? sacc[kb][j] : -INFINITY;
+                        const bool vis = p.mask == RF_MASK_SLIDING ? (off <= rel_hi && off >= rel_lo) : off <= rel_hi;
+                        sacc[kb][j] = vis ? sacc[kb][j] : -INFINITY;
                     }
             }
 

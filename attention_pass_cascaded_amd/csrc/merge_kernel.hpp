@@ -2,8 +2,11 @@
 // and level-2 sum of the cascade applied over chunks, RedFuser Fig. 4):
 //   M = max_c lse_c,  lse = M + ln sum_c exp(lse_c - M),
 //   O = sum_c exp(lse_c - lse) O_c,  rounded once to the output dtype.
-// One wavefront per row: the chunk loop reads each chunk's D floats with
-// consecutive lanes on consecutive d (coalesced).
+// One work-group per row.  Every thread first folds the row's chunk lse values
+// (broadcast reads) into the running max and rescaled sum; then the threads
+// split the chunks into NSL slices, each thread streaming 4 consecutive d of
+// its chunks with 16-byte loads (all in flight at once), and the slices are
+// summed through LDS.
 #pragma once
 
 #include "common.hpp"
@@ -11,7 +14,6 @@
 namespace rf {
 
 constexpr int MRG_THREADS = 256;
-constexpr int MRG_ROWS = MRG_THREADS / 64;
 
 template <typename T, int D>
 __global__ __launch_bounds__(MRG_THREADS) void lse_merge_kernel(const float* __restrict__ o_part,
@@ -20,39 +22,62 @@ __global__ __launch_bounds__(MRG_THREADS) void lse_merge_kernel(const float* __r
                                                                 int rows, int S) {
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr float LN2 = 0.6931471805599453f;
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const size_t row = (size_t)blockIdx.x * MRG_ROWS + (threadIdx.x >> 6);
-    if (row >= (size_t)rows) return;
+    constexpr int TPS = D / 4;               // threads per slice (4 d each)
+    constexpr int NSL = MRG_THREADS / TPS;   // chunk slices
+    __shared__ float4 part[NSL][TPS];
+
+    const size_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int slice = tid / TPS;
+    const int d4 = tid % TPS;
     const float* lp = lse_part + row * S;
 
-    float M = -INFINITY;
-    for (int cidx = lane; cidx < S; cidx += 64) M = fmaxf(M, lp[cidx]);
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w, 64));
-    const bool live = M != -INFINITY;
-    const float Mu = live ? M : 0.f;
+    // level 1 and level 2 over the chunks, folded incrementally (log2 units)
+    float m = -INFINITY, tot = 0.f;
+    for (int c = 0; c < S; ++c) {
+        const float x = lp[c] * LOG2E;
+        const float mn = fmaxf(m, x);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        tot = tot * fast_exp2(m - mu) + fast_exp2(x - mu);
+        m = mn;
+    }
+    const bool live = m != -INFINITY;
+    const float lse2 = live ? m + fast_log2(tot) : 0.f;
 
-    float tot = 0.f;
-    for (int cidx = lane; cidx < S; cidx += 64) tot += fast_exp2((lp[cidx] - Mu) * LOG2E);
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) tot += __shfl_xor(tot, w, 64);
-    const float lse_row = live ? Mu + fast_log2(tot) * LN2 : -INFINITY;
-
-    float acc[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {
-        const float* op = o_part + row * S * D;
-        for (int cidx = 0; cidx < S; ++cidx) {
-            const float w = fast_exp2((lp[cidx] - lse_row) * LOG2E);  // empty chunk: exp2(-inf) = 0
-#pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, op[(size_t)cidx * D + lane + 64 * i], acc[i]);
+        const float4* op = (const float4*)(o_part + row * (size_t)S * D) + d4;
+#pragma unroll 8
+        for (int c = slice; c < S; c += NSL) {
+            const float w = fast_exp2(fmaf(lp[c], LOG2E, -lse2));  // empty chunk: 2^-inf = 0
+            const float4 x = op[(size_t)c * TPS];
+            acc.x = fmaf(w, x.x, acc.x);
+            acc.y = fmaf(w, x.y, acc.y);
+            acc.z = fmaf(w, x.z, acc.z);
+            acc.w = fmaf(w, x.w, acc.w);
         }
     }
+    part[slice][d4] = acc;
+    __syncthreads();
+    if (slice == 0) {
+        float4 s = part[0][d4];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[row * D + lane + 64 * i] = from_f32<T>(acc[i]);
-    if (lane == 0) lse[row] = lse_row;
+        for (int k = 1; k < NSL; ++k) {
+            const float4 y = part[k][d4];
+            s.x += y.x;
+            s.y += y.y;
+            s.z += y.z;
+            s.w += y.w;
+        }
+        typedef T T4 __attribute__((ext_vector_type(4)));
+        T4 w;
+        w[0] = from_f32<T>(s.x);
+        w[1] = from_f32<T>(s.y);
+        w[2] = from_f32<T>(s.z);
+        w[3] = from_f32<T>(s.w);
+        *(T4*)(o + row * D + 4 * d4) = w;
+        if (d4 == 0) lse[row] = live ? lse2 * LN2 : -INFINITY;
+    }
 }
 
 }  // namespace rf

@@ -12,7 +12,9 @@ Work counted (algorithmic, not what the kernels happen to execute):
   flops = 4 * D per visible (query, key) pair (Q.K^T and P.V, 2 each);
   bytes = q, k, v read once + o written once (+ lse, float32).
 Timing: torch.cuda.Event on the stream the kernels are launched on (the
-current stream), W untimed warmup steps, then K timed steps back to back.
+current stream).  Each workload first runs untimed for 0.3 s so the GPU clock
+reaches its loaded steady state, then W untimed warmup steps, then K timed
+steps back to back.
 """
 from __future__ import annotations
 
@@ -41,7 +43,7 @@ PEAK_HBM_GBS = 8000.0
 # while these are unchanged since the counters were taken.
 KERNEL_SOURCES = {
     "fwd": ["attention_pass_cascaded_amd/csrc/fwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
-    "decode": ["attention_pass_cascaded_amd/csrc/decode_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "decode": ["attention_pass_cascaded_amd/csrc/decode_mfma_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
 }
 
 
@@ -91,8 +93,17 @@ def traffic_from_profiles(kind: str, workload: str):
     return float(m.group(1))
 
 
+CLOCK_WARM_S = 0.3  # untimed run-in before the warmup steps: lets the GPU clock settle
+
+
 def time_loop(fn, steps: int, warmup: int) -> float:
+    """ms per call: a clock run-in, `warmup` untimed calls, then `steps` timed calls."""
     import torch
+    t_end = time.perf_counter() + CLOCK_WARM_S
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -174,16 +185,20 @@ def run_decode(w, steps, warmup):
 
 
 def cpu_baseline(w, q, k, v, heads: int):
-    """The fp64 oracle on a bounded sample: batch 0, the first `heads` heads."""
+    """The fp64 oracle on the workload (or batch 0's first `heads` heads)."""
     import oracle
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    qs = q[:1, :heads].cpu()
-    ks = k[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
-    vs = v[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
+    if heads <= 0:
+        qs, ks, vs = q.cpu(), k.cpu(), v.cpu()
+        heads = w.B * w.Hq
+    else:
+        qs = q[:1, :heads].cpu()
+        ks = k[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
+        vs = v[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
     t0 = time.perf_counter()
     if threadpool_limits is not None:
         with threadpool_limits(limits=cores):
@@ -193,8 +208,9 @@ def cpu_baseline(w, q, k, v, heads: int):
     dt = time.perf_counter() - t0
     flops = 4.0 * w.D * visible_pairs(w.Nq, w.Nk, w.mask, w.window) * heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"batch 0, heads 0..{heads - 1} of {w.name} ({heads}/{w.B * w.Hq} of the workload, "
-                      f"{flops / 1e9:.2f} GFLOP) in {dt:.1f} s, float64 numpy"}
+            "sample": (f"whole {w.name} workload" if heads == w.B * w.Hq else
+                       f"batch 0, heads 0..{heads - 1} of {w.name} ({heads}/{w.B * w.Hq} of the workload)")
+                      + f", {flops / 1e9:.2f} GFLOP in {dt:.1f} s, float64 numpy three-pass oracle"}
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -211,11 +227,11 @@ def copy_calibration(nbytes: int, steps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default=None, help="time a single workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads of batch 0 for the oracle (0: whole workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
 
@@ -243,7 +259,7 @@ def main():
     w = by_name(HEADLINE)
     head, (q, k, v) = run_prefill(w, args.steps, args.warmup)
     print(f"# headline {w.name}: {head['ms']:.4f} ms, {head['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    dec = run_decode(by_name(DECODE), max(5, args.steps // 2), max(2, args.warmup // 2))
+    dec = run_decode(by_name(DECODE), args.steps, args.warmup)
     print(f"# decode: {dec['ms_per_step']:.4f} ms, {dec['value']:.0f} GB/s", file=sys.stderr, flush=True)
     variants = {}
     for name in VARIANTS:

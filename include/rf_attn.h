@@ -113,7 +113,8 @@ size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits);
  *   o = sum_c exp(lse_c - lse) * o_c, rounded once to out_dtype.
  * o_part float32 [rows, S, D], lse_part float32 [rows, S]; o [rows, D] of
  * out_dtype, lse float32 [rows].  Rows whose chunks are all empty get o = 0,
- * lse = -inf.  rows >= 0, 1 <= num_splits <= 4096, D in {64, 128}.
+ * lse = -inf.  rows >= 0 (< 2^31), 1 <= num_splits <= 4096, D in {64, 128}.
+ * o_part must be 16-byte aligned and o aligned to 4 of its elements.
  */
 rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                        int rows, int num_splits, int D, int out_dtype, hipStream_t stream);
