@@ -102,7 +102,8 @@ rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     if ((size_t)B * Nq == 0) return RF_OK;
     if (!o || !lse) return fail(RF_ERR_INVALID_ARG, "o and lse are required");
     if (!aligned16(o) || ((uintptr_t)lse & 3u)) return fail(RF_ERR_INVALID_ARG, "o must be 16-byte aligned, lse 4-byte aligned");
-    if ((Nq + rf::FWD_BM - 1) / rf::FWD_BM > 65535) return fail(RF_ERR_INVALID_ARG, "Nq too large");
+    if ((size_t)B * Hq * ((Nq + rf::FWD_BM - 1) / rf::FWD_BM) > 0x7fffffffu)
+        return fail(RF_ERR_INVALID_ARG, "B*Hq*ceil(Nq/128) too large");
     p.o = o;
     p.lse = lse;
     return hip_status(launch_fwd(p, dtype, stream), "rf_attn_fwd launch");
@@ -133,8 +134,8 @@ rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float
     const int max_rows = dtype == RF_F32 ? rf::DEC_MAX_ROWS_F32 : rf::DEC_MAX_ROWS_16;
     if (rows <= max_rows && Hkv <= 65535 && B <= 65535)
         return hip_status(launch_decode(p, dtype, stream), "rf_attn_splitkv_fwd decode launch");
-    if ((Nq + rf::FWD_BM - 1) / rf::FWD_BM > 65535) return fail(RF_ERR_INVALID_ARG, "Nq too large");
-    if ((size_t)B * Hq * num_splits > 0x7fffffffu) return fail(RF_ERR_INVALID_ARG, "B*Hq*num_splits too large");
+    if ((size_t)B * Hq * num_splits * ((Nq + rf::FWD_BM - 1) / rf::FWD_BM) > 0x7fffffffu)
+        return fail(RF_ERR_INVALID_ARG, "B*Hq*num_splits*ceil(Nq/128) too large");
     return hip_status(launch_fwd(p, dtype, stream), "rf_attn_splitkv_fwd launch");
 }
 

@@ -16,6 +16,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// MI355X: 8 accelerator complex dies (XCDs) of 32 CUs, each with its own L2.
+constexpr int NUM_XCD = 8;
+
 // Fused forward work-group: 4 wavefronts of 32 query rows each.
 constexpr int FWD_WAVES = 4;
 constexpr int FWD_THREADS = 64 * FWD_WAVES;

@@ -80,13 +80,32 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    // x = (b * Hq + h) * S + split; y = query block, heaviest (latest) first
-    int bx = blockIdx.x;
+    // Work-group order (one-dimensional grid of B*Hq*S*nqb).
+    //  causal: every head's heaviest (latest) query blocks first, then lighter
+    //    ones, so the uneven blocks balance across the CUs;
+    //  no mask / sliding window (every block costs the same): the dispatcher
+    //    deals work-groups round-robin over the XCDs (each with its own L2), so
+    //    renumber to give every XCD a contiguous run of one head's query blocks
+    //    and keep the K/V tiles that neighbouring blocks share in its L2.
+    const int nqb = (p.Nq + FWD_BM - 1) / FWD_BM;
+    const int G = gridDim.x;
+    const int pid = blockIdx.x;
+    int qb, bx;  // bx = (b * Hq + h) * S + split
+    if (p.mask == RF_MASK_CAUSAL) {
+        const int heads = G / nqb;
+        qb = nqb - 1 - pid / heads;
+        bx = pid % heads;
+    } else {
+        const int xcd = pid % NUM_XCD, local = pid / NUM_XCD;
+        const int per = G / NUM_XCD, rem = G % NUM_XCD;
+        const int L = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+        qb = L % nqb;
+        bx = L / nqb;
+    }
     const int split = bx % p.num_splits;
     bx /= p.num_splits;
     const int h = bx % p.Hq;
     const int b = bx / p.Hq;
-    const int qb = gridDim.y - 1 - blockIdx.y;
     const int q0 = qb * FWD_BM;
     const int g = h / (p.Hq / p.Hkv);
     const int pos_off = p.Nk - p.Nq;

@@ -10,7 +10,7 @@ namespace rf {
 
 template <typename T, int D, bool ROPE>
 hipError_t fwd_launch_one(const AttnParams& p, hipStream_t s) {
-    dim3 grid((unsigned)(p.B * p.Hq * p.num_splits), (unsigned)((p.Nq + FWD_BM - 1) / FWD_BM));
+    dim3 grid((unsigned)(p.B * p.Hq * p.num_splits * ((p.Nq + FWD_BM - 1) / FWD_BM)));
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE>), grid, dim3(FWD_THREADS), 0, s, p);
     return hipGetLastError();
 }
