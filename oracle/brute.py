@@ -36,8 +36,12 @@ def _visible(p, j, mask, window):
     return p - window < j <= p
 
 
-def brute_attention(q, k, v, scale, mask="none", window=0, rope_base=0.0):
-    """q: nested lists [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D].  Returns (O, LSE) lists."""
+def brute_attention(q, k, v, scale, mask="none", window=0, rope_base=0.0, alibi_slopes=None):
+    """q: nested lists [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D].  Returns (O, LSE) lists.
+
+    ALiBi: exp(s) is multiplied by exp(-slope_h * |p - j|), the same as adding
+    the bias to the score.
+    """
     B, Hq, Nq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv, Nk = len(k[0]), len(k[0][0])
     G = Hq // Hkv
@@ -60,7 +64,10 @@ def brute_attention(q, k, v, scale, mask="none", window=0, rope_base=0.0):
                     if rope_base > 0:
                         kj = _rot(kj, j, rope_base)
                     s = scale * math.fsum(qi[d] * kj[d] for d in range(D))
-                    ex.append(math.exp(s))
+                    w = math.exp(s)
+                    if alibi_slopes is not None:
+                        w *= math.exp(-alibi_slopes[h] * abs(p - j))
+                    ex.append(w)
                 z = math.fsum(ex)
                 for d in range(D):
                     O[b][h][i][d] = math.fsum(ex[n] * v[b][g][j][d] for n, j in enumerate(keys)) / z

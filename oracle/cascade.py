@@ -26,7 +26,10 @@ Readings where the pages are silent (each is also listed in the design notes):
     = position * theta_i, rotation by +angle; applied to q and k only, before
     the scale; V is not rotated;
   * GQA: query head h reads KV head h // (Hq // Hkv);
-  * split-KV chunk c covers keys [c*ceil(Nk/S), min(Nk, (c+1)*ceil(Nk/S))).
+  * split-KV chunk c covers keys [c*ceil(Nk/S), min(Nk, (c+1)*ceil(Nk/S)));
+  * ALiBi (AttnFuse Table 6 names "Causal+ALiBi" only): a per-head slope m_h
+    adds the bias -m_h * |p_i - j| to the scaled score of every visible pair;
+    the slopes are an input.
 """
 from __future__ import annotations
 
@@ -103,11 +106,19 @@ def _key_span(p_lo: int, p_hi: int, Nk: int, mask: str, window: int):
     return lo, max(lo, hi)
 
 
+def alibi_bias(slope: float, pos_q, pos_k) -> np.ndarray:
+    """ALiBi bias -slope * |p_i - j| for query positions pos_q and key positions pos_k."""
+    pq = np.asarray(pos_q, dtype=np.float64)[:, None]
+    pk = np.asarray(pos_k, dtype=np.float64)[None, :]
+    return -float(slope) * np.abs(pq - pk)
+
+
 # --------------------------------------------------------------------------
 # The unfused three-pass cascade (RedFuser abstract, Fig. 3a; guide Pattern 4)
 # --------------------------------------------------------------------------
-def _three_pass(qr, kr, v, vis, scale):
-    """One head, a block of query rows.  qr [R, D], kr [K, D], v [K, D], vis [R, K].
+def _three_pass(qr, kr, v, vis, scale, bias=None):
+    """One head, a block of query rows.  qr [R, D], kr [K, D], v [K, D], vis [R, K],
+    bias [R, K] (ALiBi) or None.
 
     Level 1 (combine = max):        m_i = max_j s_ij
     Level 2 (combine = +):          l_i = sum_j exp(s_ij - m_i)
@@ -115,6 +126,8 @@ def _three_pass(qr, kr, v, vis, scale):
     Each level is a full pass over the scores that reads the previous level's result.
     """
     s = scale * (qr @ kr.T)
+    if bias is not None:
+        s = s + bias
     s = np.where(vis, s, NEG_INF)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)   # pass 1
     empty = ~np.isfinite(m)
@@ -128,7 +141,7 @@ def _three_pass(qr, kr, v, vis, scale):
     return o, lse
 
 
-def softmax_probs(q, k, scale, mask="none", window=0, rope_base=0.0, b=0, h=0):
+def softmax_probs(q, k, scale, mask="none", window=0, rope_base=0.0, b=0, h=0, alibi_slopes=None):
     """Dense P = softmax(masked scaled scores) for one head, via the first two passes.
 
     Returned for the invariant that every row with a visible key sums to one.
@@ -140,7 +153,10 @@ def softmax_probs(q, k, scale, mask="none", window=0, rope_base=0.0, b=0, h=0):
     qr, kr = q[b, h], k[b, g]
     if rope_base > 0:
         qr, kr = rope_rotate(qr, pq, rope_base), rope_rotate(kr, pk, rope_base)
-    s = np.where(visible_mask(pq, pk, mask, window), scale * (qr @ kr.T), NEG_INF)
+    sc = scale * (qr @ kr.T)
+    if alibi_slopes is not None:
+        sc = sc + alibi_bias(alibi_slopes[h], pq, pk)
+    s = np.where(visible_mask(pq, pk, mask, window), sc, NEG_INF)
     m = s.max(axis=1)
     m_safe = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m_safe[:, None])
@@ -149,7 +165,7 @@ def softmax_probs(q, k, scale, mask="none", window=0, rope_base=0.0, b=0, h=0):
 
 
 def attention(q, k, v, scale, mask="none", window=0, rope_base=0.0,
-              key_lo=0, key_hi=None, row_block=512):
+              key_lo=0, key_hi=None, row_block=512, alibi_slopes=None):
     """Full forward: returns (O [B,Hq,Nq,D], LSE [B,Hq,Nq]) in float64.
 
     Works one (b, h) at a time, in blocks of query rows, over exactly the key
@@ -188,12 +204,13 @@ def attention(q, k, v, scale, mask="none", window=0, rope_base=0.0,
                 if hi <= lo:
                     continue  # no visible key: O = 0, LSE = -inf already
                 vis = visible_mask(pq[r0:r1], np.arange(lo, hi), mask, window)
-                o, lse = _three_pass(qh[r0:r1], kr[lo:hi], v[b, g, lo:hi], vis, scale)
+                bias = None if alibi_slopes is None else alibi_bias(alibi_slopes[h], pq[r0:r1], np.arange(lo, hi))
+                o, lse = _three_pass(qh[r0:r1], kr[lo:hi], v[b, g, lo:hi], vis, scale, bias)
                 O[b, h, r0:r1], L[b, h, r0:r1] = o, lse
     return O, L
 
 
-def attention_rows(q, k, v, scale, rows, mask="none", window=0, rope_base=0.0):
+def attention_rows(q, k, v, scale, rows, mask="none", window=0, rope_base=0.0, alibi_slopes=None):
     """O and LSE for selected rows only: ``rows`` is an iterable of (b, h, i).
 
     Returns (O [R, D], LSE [R]) in the order given.  Each row is the same
@@ -219,7 +236,8 @@ def attention_rows(q, k, v, scale, rows, mask="none", window=0, rope_base=0.0):
             qi = rope_rotate(qi, np.array([p]), rope_base)
             kr = rope_rotate(kr, np.arange(lo, hi), rope_base)
         vis = visible_mask(np.array([p]), np.arange(lo, hi), mask, window)
-        o, lse = _three_pass(qi, kr, _f64(vf[b, g, lo:hi]), vis, scale)
+        bias = None if alibi_slopes is None else alibi_bias(alibi_slopes[h], [p], np.arange(lo, hi))
+        o, lse = _three_pass(qi, kr, _f64(vf[b, g, lo:hi]), vis, scale, bias)
         out_o[n], out_l[n] = o[0], lse[0]
     return out_o, out_l
 
@@ -228,7 +246,7 @@ def attention_rows(q, k, v, scale, rows, mask="none", window=0, rope_base=0.0):
 # Incremental form (RedFuser Fig. 4b; operator pairs of Table 1)
 # --------------------------------------------------------------------------
 def attention_incremental(q, k, v, scale, mask="none", window=0, rope_base=0.0,
-                          tile=64, order=None):
+                          tile=64, order=None, alibi_slopes=None):
     """Single pass over key tiles, keeping only the running (m, l, O) per row.
 
     For each tile T of keys, with s the tile's masked scaled scores:
@@ -260,7 +278,10 @@ def attention_incremental(q, k, v, scale, mask="none", window=0, rope_base=0.0,
             acc = np.zeros((Nq, D))
             for T in tiles:
                 vis = visible_mask(pq, T, mask, window)
-                s = np.where(vis, scale * (qh @ kh[T].T), NEG_INF)
+                sc = scale * (qh @ kh[T].T)
+                if alibi_slopes is not None:
+                    sc = sc + alibi_bias(alibi_slopes[h], pq, T)
+                s = np.where(vis, sc, NEG_INF)
                 m_new = np.maximum(m, s.max(axis=1))
                 live = np.isfinite(m_new)
                 m_ref = np.where(live, m_new, 0.0)
@@ -284,7 +305,7 @@ def split_bounds(Nk: int, num_splits: int):
     return [(c * step, min(Nk, (c + 1) * step)) for c in range(num_splits)]
 
 
-def split_partials(q, k, v, scale, num_splits, mask="none", window=0, rope_base=0.0):
+def split_partials(q, k, v, scale, num_splits, mask="none", window=0, rope_base=0.0, alibi_slopes=None):
     """Per-chunk normalised partials: (O_c [B,Hq,Nq,S,D], lse_c [B,Hq,Nq,S]).
 
     Chunk c is the three-pass definition restricted to its key range; a chunk
@@ -298,7 +319,8 @@ def split_partials(q, k, v, scale, num_splits, mask="none", window=0, rope_base=
     for c, (lo, hi) in enumerate(split_bounds(Nk, num_splits)):
         if hi <= lo:
             continue
-        o, lse = attention(q, k, v, scale, mask, window, rope_base, key_lo=lo, key_hi=hi)
+        o, lse = attention(q, k, v, scale, mask, window, rope_base, key_lo=lo, key_hi=hi,
+                           alibi_slopes=alibi_slopes)
         Op[:, :, :, c], Lp[:, :, :, c] = o, lse
     return Op, Lp
 
@@ -336,5 +358,5 @@ def rounding_floor(o64: np.ndarray, dtype) -> float:
 __all__ = [
     "attention", "attention_rows", "attention_incremental", "split_partials",
     "split_bounds", "lse_merge", "rope_rotate", "visible_mask", "query_positions",
-    "softmax_probs", "rounding_floor",
+    "softmax_probs", "rounding_floor", "alibi_bias",
 ]

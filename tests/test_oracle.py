@@ -284,3 +284,65 @@ def test_oracle_consumes_low_precision_inputs_exactly():
     o2, l2 = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.25, "causal")
     close(o1, o2, rtol=0, atol=0)
     close(l1, l2, rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- ALiBi
+ALIBI_CASES = [
+    (1, 2, 2, 7, 7, 4, "causal", 0, 0.0),
+    (1, 4, 2, 6, 9, 4, "none", 0, 0.0),
+    (1, 2, 1, 8, 8, 4, "sliding", 3, 10000.0),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,D,mask,window,base", ALIBI_CASES)
+def test_alibi_matches_brute_force(B, Hq, Hkv, Nq, Nk, D, mask, window, base):
+    from workloads import alibi_slopes
+    seed = zlib.crc32(repr(("alibi", B, Hq, Nq, Nk, mask)).encode())
+    q, k, v = rnd((B, Hq, Nq, D), seed), rnd((B, Hkv, Nk, D), seed + 1), rnd((B, Hkv, Nk, D), seed + 2)
+    sl = alibi_slopes(Hq)
+    o, lse = oracle.attention(q, k, v, 0.5, mask, window, base, alibi_slopes=sl)
+    ob, lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), 0.5, mask, window, base, alibi_slopes=sl)
+    close(o, ob)
+    close(lse, lb)
+    oi, li = oracle.attention_incremental(q, k, v, 0.5, mask, window, base, tile=3, alibi_slopes=sl)
+    close(oi, o)
+    close(li, lse)
+    op, lp = oracle.split_partials(q, k, v, 0.5, 3, mask, window, base, alibi_slopes=sl)
+    om, lm = oracle.lse_merge(op, lp)
+    close(om, o)
+    close(lm, lse)
+    rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(Nq)]
+    orow, lrow = oracle.attention_rows(q, k, v, 0.5, rows, mask, window, base, alibi_slopes=sl)
+    close(orow, o.reshape(-1, D))
+    close(lrow, lse.reshape(-1))
+
+
+def test_alibi_zero_scores_give_geometric_weights():
+    """q = 0: weights exp(-m (p - j)) / sum, a closed form; V = identity picks them out."""
+    N, m = 5, 0.7
+    q = np.zeros((1, 1, N, N))
+    k = rnd((1, 1, N, N), 120)
+    v = np.eye(N)[None, None]
+    o, lse = oracle.attention(q, k, v, 1.0, "causal", alibi_slopes=[m])
+    for i in range(N):
+        w = np.array([math.exp(-m * (i - j)) for j in range(i + 1)])
+        close(o[0, 0, i, : i + 1], w / w.sum(), rtol=1e-14, atol=1e-15)
+        close(o[0, 0, i, i + 1:], np.zeros(N - i - 1), rtol=0, atol=0)
+        close(lse[0, 0, i], math.log(w.sum()), rtol=1e-14, atol=1e-15)
+
+
+def test_alibi_zero_slope_is_plain_attention_and_matches_sdpa():
+    q, k, v = rnd((1, 3, 10, 8), 121), rnd((1, 3, 10, 8), 122), rnd((1, 3, 10, 8), 123)
+    o0, l0 = oracle.attention(q, k, v, 0.3, "causal")
+    o1, l1 = oracle.attention(q, k, v, 0.3, "causal", alibi_slopes=[0.0, 0.0, 0.0])
+    close(o1, o0)
+    close(l1, l0)
+    sl = [0.5, 0.25, 0.125]
+    o2, _ = oracle.attention(q, k, v, 0.3, "causal", alibi_slopes=sl)
+    pos = np.arange(10)
+    bias = np.stack([A.alibi_bias(s, pos, pos) for s in sl])[None]
+    vis = A.visible_mask(pos, pos, "causal")
+    mask = torch.from_numpy(np.where(vis, bias, -np.inf))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.3)
+    close(o2, ref.numpy(), rtol=1e-11, atol=1e-13)

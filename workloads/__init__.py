@@ -26,7 +26,7 @@ import math
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal"]
+__all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal", "alibi_slopes"]
 
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -99,6 +99,11 @@ def gen_qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed, device="cpu"):
     k = gen_normal((B, Hkv, Nk, D), dtype, g)
     v = gen_normal((B, Hkv, Nk, D), dtype, g)
     return q, k, v
+
+
+def alibi_slopes(H: int):
+    """The usual geometric ALiBi slope schedule 2^(-8h/H), h = 1..H (a fixed input)."""
+    return [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
 
 
 def gen_workload(w: Workload, seed: int | None = None, device="cpu"):
