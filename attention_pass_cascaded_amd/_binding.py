@@ -21,8 +21,8 @@ RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP = 0, 1, 2, 3
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
-EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_splitkv_workspace_bytes",
-            "rf_lse_merge", "rf_status_string", "rf_last_error")
+EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
+            "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_status_string", "rf_last_error")
 
 
 class RFError(RuntimeError):
@@ -48,6 +48,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_attn_fwd.restype = i
     lib.rf_attn_splitkv_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, i, i, vp]
     lib.rf_attn_splitkv_fwd.restype = i
+    lib.rf_attn_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, vp, i, vp]
+    lib.rf_attn_fwd_alibi.restype = i
+    lib.rf_attn_splitkv_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, vp, i, i, vp]
+    lib.rf_attn_splitkv_fwd_alibi.restype = i
     lib.rf_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.rf_splitkv_workspace_bytes.restype = sz
     lib.rf_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
@@ -95,17 +99,32 @@ def _scale(scale, D):
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
 
-def fwd(q, k, v, scale=None, mask="none", window=0, rope_base=0.0, out=None, lse=None):
-    """Fused forward.  Returns (o [B,Hq,Nq,D] in q.dtype, lse [B,Hq,Nq] float32)."""
+def _slopes(alibi_slopes, Hq, device):
+    """ALiBi slopes as a device float32 [Hq] tensor (kept alive by the caller frame)."""
+    if alibi_slopes is None:
+        return None
+    t = torch.as_tensor(alibi_slopes, dtype=torch.float32).to(device).contiguous()
+    if t.shape != (Hq,):
+        raise ValueError(f"alibi_slopes must have Hq={Hq} entries")
+    return t
+
+
+def fwd(q, k, v, scale=None, mask="none", window=0, rope_base=0.0, out=None, lse=None,
+        alibi_slopes=None):
+    """Fused forward.  Returns (o [B,Hq,Nq,D] in q.dtype, lse [B,Hq,Nq] float32).
+
+    alibi_slopes: optional per-query-head slopes (sequence or tensor of Hq floats).
+    """
     B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    slopes = _slopes(alibi_slopes, Hq, q.device)
     lib = load_library()
-    _check(lib.rf_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, D,
-                           _scale(scale, D), _MASK[mask], int(window), float(rope_base),
-                           _DTYPE[q.dtype], _stream(q)))
+    _check(lib.rf_attn_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, D,
+                                 _scale(scale, D), _MASK[mask], int(window), float(rope_base), _ptr(slopes),
+                                 _DTYPE[q.dtype], _stream(q)))
     return out, lse
 
 
@@ -114,7 +133,7 @@ def workspace_bytes(B, Hq, Nq, D, num_splits) -> int:
 
 
 def splitkv_fwd(q, k, v, num_splits, scale=None, mask="none", window=0, rope_base=0.0,
-                o_part=None, lse_part=None):
+                o_part=None, lse_part=None, alibi_slopes=None):
     """Split-KV partials: (o_part [B,Hq,Nq,S,D] float32, lse_part [B,Hq,Nq,S] float32)."""
     B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
     S = int(num_splits)
@@ -122,10 +141,11 @@ def splitkv_fwd(q, k, v, num_splits, scale=None, mask="none", window=0, rope_bas
         o_part = torch.empty((B, Hq, Nq, S, D), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((B, Hq, Nq, S), dtype=torch.float32, device=q.device)
+    slopes = _slopes(alibi_slopes, Hq, q.device)
     lib = load_library()
-    _check(lib.rf_attn_splitkv_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part),
-                                   B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask], int(window),
-                                   float(rope_base), S, _DTYPE[q.dtype], _stream(q)))
+    _check(lib.rf_attn_splitkv_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part),
+                                         B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask], int(window),
+                                         float(rope_base), _ptr(slopes), S, _DTYPE[q.dtype], _stream(q)))
     return o_part, lse_part
 
 
@@ -150,7 +170,7 @@ def lse_merge(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
     return out, lse
 
 
-def decode(q, k, v, num_splits=64, scale=None, mask="none", window=0, rope_base=0.0):
+def decode(q, k, v, num_splits=64, scale=None, mask="none", window=0, rope_base=0.0, alibi_slopes=None):
     """Split-KV attention: partials then log-sum-exp merge.  Returns (o, lse) like fwd."""
-    op, lp = splitkv_fwd(q, k, v, num_splits, scale, mask, window, rope_base)
+    op, lp = splitkv_fwd(q, k, v, num_splits, scale, mask, window, rope_base, alibi_slopes=alibi_slopes)
     return lse_merge(op, lp, out_dtype=q.dtype)

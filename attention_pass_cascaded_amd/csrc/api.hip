@@ -93,12 +93,13 @@ hipError_t launch_decode(const rf::AttnParams& p, int dtype, hipStream_t s) {
 
 extern "C" {
 
-rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                      int Hkv, int Nq, int Nk, int D, float scale, int mask_kind, int window,
-                      float rope_base, int dtype, hipStream_t stream) {
+rf_status rf_attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                            int Hq, int Hkv, int Nq, int Nk, int D, float scale, int mask_kind, int window,
+                            float rope_base, const float* alibi_slopes, int dtype, hipStream_t stream) {
     rf::AttnParams p;
     rf_status st = check_attn(q, k, v, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base, dtype, p);
     if (st != RF_OK) return st;
+    if (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) return fail(RF_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if ((size_t)B * Nq == 0) return RF_OK;
     if (!o || !lse) return fail(RF_ERR_INVALID_ARG, "o and lse are required");
     if (!aligned16(o) || ((uintptr_t)lse & 3u)) return fail(RF_ERR_INVALID_ARG, "o must be 16-byte aligned, lse 4-byte aligned");
@@ -106,7 +107,15 @@ rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
         return fail(RF_ERR_INVALID_ARG, "B*Hq*ceil(Nq/128) too large");
     p.o = o;
     p.lse = lse;
+    p.alibi = alibi_slopes;
     return hip_status(launch_fwd(p, dtype, stream), "rf_attn_fwd launch");
+}
+
+rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int D, float scale, int mask_kind, int window,
+                      float rope_base, int dtype, hipStream_t stream) {
+    return rf_attn_fwd_alibi(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base,
+                             nullptr, dtype, stream);
 }
 
 size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits) {
@@ -114,12 +123,14 @@ size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits) 
     return (size_t)B * Hq * Nq * num_splits * (size_t)(D + 1) * sizeof(float);
 }
 
-rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
-                              int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale, int mask_kind,
-                              int window, float rope_base, int num_splits, int dtype, hipStream_t stream) {
+rf_status rf_attn_splitkv_fwd_alibi(const void* q, const void* k, const void* v, float* o_part,
+                                    float* lse_part, int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+                                    int mask_kind, int window, float rope_base, const float* alibi_slopes,
+                                    int num_splits, int dtype, hipStream_t stream) {
     rf::AttnParams p;
     rf_status st = check_attn(q, k, v, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base, dtype, p);
     if (st != RF_OK) return st;
+    if (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) return fail(RF_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (num_splits < 1 || num_splits > 4096) return fail(RF_ERR_INVALID_ARG, "num_splits must be in [1, 4096] (got %d)", num_splits);
     if ((size_t)B * Nq == 0) return RF_OK;
     if (!o_part || !lse_part) return fail(RF_ERR_INVALID_ARG, "o_part and lse_part are required");
@@ -130,6 +141,7 @@ rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float
     p.num_splits = num_splits;
     p.split_len = (Nk + num_splits - 1) / num_splits;
     p.split_mode = 1;
+    p.alibi = alibi_slopes;
     const int rows = (Hq / Hkv) * Nq;
     const int max_rows = dtype == RF_F32 ? rf::DEC_MAX_ROWS_F32 : rf::DEC_MAX_ROWS_16;
     if (rows <= max_rows && Hkv <= 65535 && B <= 65535)
@@ -137,6 +149,13 @@ rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float
     if ((size_t)B * Hq * num_splits * ((Nq + rf::FWD_BM - 1) / rf::FWD_BM) > 0x7fffffffu)
         return fail(RF_ERR_INVALID_ARG, "B*Hq*num_splits*ceil(Nq/128) too large");
     return hip_status(launch_fwd(p, dtype, stream), "rf_attn_splitkv_fwd launch");
+}
+
+rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale, int mask_kind,
+                              int window, float rope_base, int num_splits, int dtype, hipStream_t stream) {
+    return rf_attn_splitkv_fwd_alibi(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window,
+                                     rope_base, nullptr, num_splits, dtype, stream);
 }
 
 rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int rows,

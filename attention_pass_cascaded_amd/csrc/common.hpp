@@ -38,6 +38,7 @@ struct AttnParams {
     int mask;          // rf_mask
     int window;
     float rope_base;   // > 0: RoPE on
+    const float* alibi;  // [Hq] ALiBi slopes, or null
     int num_splits;    // 1 when not splitting
     int split_len;     // keys per chunk, ceil(Nk / num_splits)
     int split_mode;    // 1: write normalised partials + chunk lse

@@ -32,7 +32,7 @@ struct DecCfg {
     static constexpr int NG = DEC_THREADS / LPR;       // key groups per work-group
 };
 
-template <typename T, int D, int R, bool ROPE>
+template <typename T, int D, int R, bool ROPE, bool ALIBI>
 __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(AttnParams p) {
     using C = DecCfg<T, D>;
     constexpr int EPL = C::EPL;
@@ -72,10 +72,12 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(AttnParams p) 
     // ---- query rows r = gi * Nq + qi (head g*G + gi, query qi), this lane's d slice
     float q[R][EPL];
     int qpos[R];
+    float slope2[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int gi = r / max(p.Nq, 1), qi = r % max(p.Nq, 1);
         qpos[r] = qi + pos_off;
+        slope2[r] = (ALIBI && r < rows) ? p.alibi[g * G + gi] * LOG2E : 0.f;
         if (r < rows) {
             const T* qrow = (const T*)p.q + (((size_t)b * p.Hq + g * G + gi) * p.Nq + qi) * D + d0;
 #pragma unroll
@@ -170,6 +172,7 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(AttnParams p) 
                 bool vis = kin[u];
                 if (p.mask != RF_MASK_NONE) vis &= key <= qpos[r];
                 if (p.mask == RF_MASK_SLIDING) vis &= key > qpos[r] - p.window;
+                if constexpr (ALIBI) a = fmaf(a, c, -slope2[r] * fabsf((float)(key - qpos[r])));
                 s[r][u] = vis ? a : -INFINITY;
             }
 
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(AttnParams p) 
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < DEC_NB; ++u) mx = fmaxf(mx, s[r][u]);
-            const float m_blk = (mx == -INFINITY) ? -INFINITY : mx * c;
+            const float m_blk = (mx == -INFINITY) ? -INFINITY : (ALIBI ? mx : mx * c);
             const float m_new = fmaxf(m_run[r], m_blk);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
             const float alpha = fast_exp2(m_run[r] - m_use);
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(AttnParams p) 
             float ls = 0.f;
 #pragma unroll
             for (int u = 0; u < DEC_NB; ++u) {
-                pu[u] = (s[r][u] == -INFINITY) ? 0.f : fast_exp2(fmaf(s[r][u], c, -m_use));
+                pu[u] = (s[r][u] == -INFINITY) ? 0.f : fast_exp2(ALIBI ? s[r][u] - m_use : fmaf(s[r][u], c, -m_use));
                 ls += pu[u];
             }
             l_run[r] = fmaf(l_run[r], alpha, ls);

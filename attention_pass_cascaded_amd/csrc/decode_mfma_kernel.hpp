@@ -38,7 +38,7 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <typename T, int D, bool ROPE>
+template <typename T, int D, bool ROPE, bool ALIBI>
 __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams p) {
     static_assert(sizeof(T) == 2, "16-bit inputs only");
     constexpr bool SPLITK = ROPE && !__is_same(T, _Float16);
@@ -89,6 +89,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
     const int my_pos = qi + pos_off;
     const int lim_hi = p.mask != RF_MASK_NONE ? min(khi - 1, my_pos) : khi - 1;
     const int lim_lo = p.mask == RF_MASK_SLIDING ? my_pos - p.window + 1 : -(1 << 30);
+    const float slope2 = ALIBI ? p.alibi[g * G + gi] * LOG2E : 0.f;  // log2 units
 
     // Q^T operand: lane holds q[row][32*ks + 8*q + i]; RoPE partner is ks +- NKS/2.
     VecT qv[NKS], qlo[SPLITK ? NKS : 1];
@@ -207,17 +208,20 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
         const int rel_hi = lim_hi - k0 - 4 * q;
         const int rel_lo = lim_lo - k0 - 4 * q;
         float mx = -INFINITY;
+        const float kd = (float)(k0 + 4 * q - my_pos);
 #pragma unroll
         for (int kgp = 0; kgp < 2; ++kgp)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int off = 16 * kgp + i;
-                sacc[kgp][i] = (off <= rel_hi && off >= rel_lo) ? sacc[kgp][i] : -INFINITY;
+                float sv = sacc[kgp][i];
+                if constexpr (ALIBI) sv = fmaf(sv, c, -slope2 * fabsf(kd + (float)off));
+                sacc[kgp][i] = (off <= rel_hi && off >= rel_lo) ? sv : -INFINITY;
                 mx = fmaxf(mx, sacc[kgp][i]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_tile = mx * c;
+        const float m_tile = ALIBI ? mx : mx * c;
 
         const bool bump = m_tile > m_ref + RESCALE_SLACK;
         if (__builtin_amdgcn_ballot_w64(bump)) {
@@ -233,7 +237,10 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
         // P^T operand: slot (q, i) holds key 16*(i/4) + 4*q + i%4 of this step
         VecT pb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = from_f32<T>(fast_exp2(fmaf(sacc[i / 4][i % 4], c, -m_sub)));
+        for (int i = 0; i < 8; ++i) {
+            const float sv = sacc[i / 4][i % 4];
+            pb[i] = from_f32<T>(fast_exp2(ALIBI ? sv - m_sub : fmaf(sv, c, -m_sub)));
+        }
         l_run = row_sum8(pb, l_run);
 
         // the V stores above must land before the transposed reads below

@@ -56,8 +56,8 @@ struct FwdCfg {
 #define RF_FWD_WAVES_D64 4
 #endif
 
-template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
+template <typename T, int D, bool ROPE, bool ALIBI>
+__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
     using C = FwdCfg<T, D, SPLITK>;
     constexpr bool F32 = C::F32;
@@ -132,6 +132,8 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 
     // log2-domain scale; kept >= 1e-30 so masked -inf scores stay -inf after
     // the multiply (scale 0 then gives exactly uniform weights).
     const float c = fmaxf(p.scale * LOG2E, 1e-30f);
+    // ALiBi: the scaled score gets -slope_h * |p_i - j|, here in log2 units
+    const float slope2 = ALIBI ? p.alibi[h] * LOG2E : 0.f;
     const size_t kv_base = ((size_t)b * p.Hkv + g) * (size_t)p.Nk * D;
     // K and V of this (batch, KV head); rows past Nk read as zeros
     const int kv_bytes = p.Nk * D * (int)sizeof(T);
@@ -347,6 +349,18 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 
                     }
             }
 
+            if constexpr (ALIBI) {
+                // scores to log2 units with the bias; key - position = kd + off
+                const float kd = (float)(k0 + 4 * hi - my_pos);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float dist = fabsf(kd + (float)(32 * kb + 8 * (j / 4) + (j % 4)));
+                        sacc[kb][j] = fmaf(sacc[kb][j], c, -slope2 * dist);
+                    }
+            }
+
             // level 1: tile max (log2 domain of the scaled scores)
             float mx = -INFINITY;
 #pragma unroll
@@ -354,7 +368,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
             mx = fmaxf(mx, swap_halves(mx));
-            const float m_tile = mx * c;
+            const float m_tile = ALIBI ? mx : mx * c;
 
             // lazy correction of levels 2 and 3: only when the max moved by > 2^8
             const bool bump = m_tile > m_ref + RESCALE_SLACK;
@@ -373,7 +387,8 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE) ? RF_FWD_WAVES_D64 
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) pr[kb][j] = fast_exp2(fmaf(sacc[kb][j], c, -m_sub));
+                for (int j = 0; j < 16; ++j)
+                    pr[kb][j] = fast_exp2(ALIBI ? sacc[kb][j] - m_sub : fmaf(sacc[kb][j], c, -m_sub));
 
             // level 3: O^T += V^T . P^T (16-bit: the rounded P also feeds l)
             if constexpr (F32) {

@@ -8,27 +8,36 @@
 
 namespace rf {
 
-template <typename T, int D, bool ROPE>
+template <typename T, int D, bool ROPE, bool ALIBI>
 hipError_t fwd_launch_one(const AttnParams& p, hipStream_t s) {
     dim3 grid((unsigned)(p.B * p.Hq * p.num_splits * ((p.Nq + FWD_BM - 1) / FWD_BM)));
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE>), grid, dim3(FWD_THREADS), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI>), grid, dim3(FWD_THREADS), 0, s, p);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t fwd_dispatch_d(const AttnParams& p, hipStream_t s) {
+    const bool rope = p.rope_base > 0.f;
+    if (p.alibi) return rope ? fwd_launch_one<T, D, true, true>(p, s) : fwd_launch_one<T, D, false, true>(p, s);
+    return rope ? fwd_launch_one<T, D, true, false>(p, s) : fwd_launch_one<T, D, false, false>(p, s);
 }
 
 template <typename T>
 hipError_t fwd_dispatch(const AttnParams& p, hipStream_t s) {
-    const bool rope = p.rope_base > 0.f;
-    if (p.D == 64) return rope ? fwd_launch_one<T, 64, true>(p, s) : fwd_launch_one<T, 64, false>(p, s);
-    return rope ? fwd_launch_one<T, 128, true>(p, s) : fwd_launch_one<T, 128, false>(p, s);
+    return p.D == 64 ? fwd_dispatch_d<T, 64>(p, s) : fwd_dispatch_d<T, 128>(p, s);
 }
 
 template <typename T, int D, int R>
 hipError_t dec_launch_rows(const AttnParams& p, hipStream_t s) {
     dim3 grid((unsigned)p.num_splits, (unsigned)p.Hkv, (unsigned)p.B);
-    if (p.rope_base > 0.f)
-        hipLaunchKernelGGL((attn_decode_kernel<T, D, R, true>), grid, dim3(DEC_THREADS), 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_decode_kernel<T, D, R, false>), grid, dim3(DEC_THREADS), 0, s, p);
+    const bool rope = p.rope_base > 0.f;
+    if (p.alibi) {
+        if (rope) hipLaunchKernelGGL((attn_decode_kernel<T, D, R, true, true>), grid, dim3(DEC_THREADS), 0, s, p);
+        else hipLaunchKernelGGL((attn_decode_kernel<T, D, R, false, true>), grid, dim3(DEC_THREADS), 0, s, p);
+    } else {
+        if (rope) hipLaunchKernelGGL((attn_decode_kernel<T, D, R, true, false>), grid, dim3(DEC_THREADS), 0, s, p);
+        else hipLaunchKernelGGL((attn_decode_kernel<T, D, R, false, false>), grid, dim3(DEC_THREADS), 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -43,10 +52,14 @@ hipError_t dec_launch_d(const AttnParams& p, hipStream_t s) {
 template <typename T, int D>
 hipError_t dec_mfma_launch_d(const AttnParams& p, hipStream_t s) {
     dim3 grid((unsigned)p.num_splits, (unsigned)p.Hkv, (unsigned)p.B);
-    if (p.rope_base > 0.f)
-        hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, true>), grid, dim3(DM_THREADS), 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, false>), grid, dim3(DM_THREADS), 0, s, p);
+    const bool rope = p.rope_base > 0.f;
+    if (p.alibi) {
+        if (rope) hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, true, true>), grid, dim3(DM_THREADS), 0, s, p);
+        else hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, false, true>), grid, dim3(DM_THREADS), 0, s, p);
+    } else {
+        if (rope) hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, true, false>), grid, dim3(DM_THREADS), 0, s, p);
+        else hipLaunchKernelGGL((attn_decode_mfma_kernel<T, D, false, false>), grid, dim3(DM_THREADS), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -101,6 +101,26 @@ rf_status rf_attn_splitkv_fwd(const void* q, const void* k, const void* v,
                               int num_splits, int dtype, hipStream_t stream);
 
 /*
+ * rf_attn_fwd_alibi / rf_attn_splitkv_fwd_alibi — the same two calls with an
+ * ALiBi bias (AttnFuse Table 6, "Causal+ALiBi"): query head h adds
+ * -alibi_slopes[h] * |p_i - j| to the scaled score of every visible pair
+ * before the softmax.  alibi_slopes: device float32 [Hq], 4-byte aligned, read
+ * by the kernels; NULL means no bias (identical to the calls above).  The
+ * slope schedule is the caller's choice (the usual one is 2^(-8h/Hq),
+ * h = 1..Hq).  Other arguments, layouts and errors as above.
+ */
+rf_status rf_attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                            float scale, int mask_kind, int window, float rope_base,
+                            const float* alibi_slopes, int dtype, hipStream_t stream);
+rf_status rf_attn_splitkv_fwd_alibi(const void* q, const void* k, const void* v,
+                                    float* o_part, float* lse_part,
+                                    int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                    float scale, int mask_kind, int window, float rope_base,
+                                    const float* alibi_slopes, int num_splits, int dtype,
+                                    hipStream_t stream);
+
+/*
  * rf_splitkv_workspace_bytes — bytes of o_part plus lse_part for the given
  * sizes: B*Hq*Nq*num_splits*(D + 1)*4.  Returns 0 for invalid sizes.
  */

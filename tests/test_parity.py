@@ -163,3 +163,54 @@ def test_merge_matches_oracle_with_empty_chunks():
     torch.cuda.synchronize()
     ro, rl = oracle.lse_merge(op, lp)
     compare(o, lse, ro, rl, 1e-5, "merge")
+
+
+# ---------------------------------------------------------------- ALiBi (AttnFuse Table 6)
+ALIBI_FWD = [
+    ("f16", 64, 1, 4, 4, 300, 300, "causal", 0, 0.0),
+    ("bf16", 128, 1, 8, 2, 150, 270, "none", 0, 0.0),
+    ("f16", 64, 1, 4, 2, 200, 200, "sliding", 60, 10000.0),
+    ("f32", 64, 1, 2, 2, 100, 100, "causal", 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("dt,D,B,Hq,Hkv,Nq,Nk,mask,window,rope", ALIBI_FWD)
+def test_fwd_alibi_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
+    from workloads import alibi_slopes
+    seed = zlib.crc32(repr(("alibi", dt, D, Hq, Nq, Nk, mask)).encode()) % 10_000
+    q, k, v = gen_qkv(B, Hq, Hkv, Nq, Nk, D, dt, seed)
+    sl = alibi_slopes(Hq)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case alibi fwd {dt} D={D} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} {mask} W={window} rope={rope}", flush=True)
+    dev = torch.device("cuda")
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dev)
+    lse = torch.full(q.shape[:3], float("nan"), device=dev)
+    rf.fwd(q.to(dev), k.to(dev), v.to(dev), scale=scale, mask=mask, window=window, rope_base=rope,
+           out=out, lse=lse, alibi_slopes=sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, scale, mask, window, rope, alibi_slopes=sl)
+    compare(out, lse, ro, rl, TOL[dt], "alibi fwd")
+
+
+ALIBI_SPLIT = [
+    ("bf16", 128, 2, 8, 2, 1, 1000, 7, "none", 0, 0.0),       # matrix-core decode kernel
+    ("f16", 64, 1, 8, 2, 2, 500, 4, "causal", 0, 0.0),        # decode kernel, 8 rows, causal
+    ("f32", 128, 1, 4, 1, 1, 333, 3, "none", 0, 0.0),         # vector-ALU decode kernel
+    ("bf16", 64, 1, 4, 4, 40, 260, 3, "causal", 0, 10000.0),  # forward kernel in split mode
+]
+
+
+@pytest.mark.parametrize("dt,D,B,Hq,Hkv,Nq,Nk,S,mask,window,rope", ALIBI_SPLIT)
+def test_splitkv_alibi_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, S, mask, window, rope):
+    from workloads import alibi_slopes
+    seed = zlib.crc32(repr(("alibi-split", dt, D, Hq, Nq, Nk, S, mask)).encode()) % 10_000
+    q, k, v = gen_qkv(B, Hq, Hkv, Nq, Nk, D, dt, seed)
+    sl = alibi_slopes(Hq)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case alibi split {dt} D={D} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} S={S} {mask} rope={rope}", flush=True)
+    dev = torch.device("cuda")
+    o, lse = rf.decode(q.to(dev), k.to(dev), v.to(dev), num_splits=S, scale=scale, mask=mask, window=window,
+                       rope_base=rope, alibi_slopes=sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, scale, mask, window, rope, alibi_slopes=sl)
+    compare(o, lse, ro, rl, TOL[dt], "alibi split")
