@@ -11,11 +11,13 @@ from ._binding import (  # noqa: F401
     RFError,
     decode,
     fwd,
+    fwd_prerotated,
+    rope_rotate,
     load_library,
     lse_merge,
     splitkv_fwd,
     workspace_bytes,
 )
 
-__all__ = ["fwd", "splitkv_fwd", "lse_merge", "decode", "workspace_bytes", "load_library",
+__all__ = ["fwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "workspace_bytes", "load_library",
            "RFError", "LIB_PATH", "EXPORTED"]

@@ -22,7 +22,8 @@ _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
 EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
-            "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_status_string", "rf_last_error")
+            "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_status_string",
+            "rf_last_error")
 
 
 class RFError(RuntimeError):
@@ -56,6 +57,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_splitkv_workspace_bytes.restype = sz
     lib.rf_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.rf_lse_merge.restype = i
+    lib.rf_rope_rotate.argtypes = [vp, vp, i, i, i, f, i, i, vp]
+    lib.rf_rope_rotate.restype = i
     lib.rf_status_string.argtypes = [i]
     lib.rf_status_string.restype = ctypes.c_char_p
     lib.rf_last_error.argtypes = []
@@ -109,12 +112,28 @@ def _slopes(alibi_slopes, Hq, device):
     return t
 
 
+# Rotation Calculus on MI355X: causal fp16 B=4 H=12 D=64 with RoPE, fused vs
+# rotate-first; the fused kernel wins below this key length (measured sweep,
+# `bench.py --rotation-sweep`).
+ROPE_FUSED_MAX_N = 2800
+
+
 def fwd(q, k, v, scale=None, mask="none", window=0, rope_base=0.0, out=None, lse=None,
-        alibi_slopes=None):
+        alibi_slopes=None, rope_mode="fused"):
     """Fused forward.  Returns (o [B,Hq,Nq,D] in q.dtype, lse [B,Hq,Nq] float32).
 
     alibi_slopes: optional per-query-head slopes (sequence or tensor of Hq floats).
+    rope_mode: "fused" rotates inside the attention kernel; "rotate_first" runs
+    rf_rope_rotate on q and k first; "auto" picks rotate-first for Nk above the
+    measured crossover when the inputs are not bfloat16 (rotating into bf16
+    would round the rotated operands, which the fused kernel avoids).
     """
+    if rope_base and rope_base > 0 and rope_mode != "fused":
+        if rope_mode not in ("auto", "rotate_first"):
+            raise ValueError(f"unknown rope_mode {rope_mode!r}")
+        if rope_mode == "rotate_first" or (k.shape[2] > ROPE_FUSED_MAX_N and q.dtype != torch.bfloat16):
+            return fwd_prerotated(q, k, v, rope_base, scale=scale, mask=mask, window=window, out=out,
+                                  lse=lse, alibi_slopes=alibi_slopes)
     B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
     if out is None:
         out = torch.empty_like(q)
@@ -168,6 +187,28 @@ def lse_merge(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
     _check(lib.rf_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), rows, S, D,
                             _DTYPE[out.dtype], _stream(o_part)))
     return out, lse
+
+
+def rope_rotate(x, base, pos_offset=0, out=None):
+    """Rotary embedding of x [B, H, N, D] at positions pos_offset + n (out may be x)."""
+    if not x.is_cuda or x.dim() != 4 or not x.is_contiguous() or x.dtype not in _DTYPE:
+        raise ValueError("x must be a contiguous [B, H, N, D] GPU tensor of float32/float16/bfloat16")
+    if out is None:
+        out = torch.empty_like(x)
+    B, H, N, D = x.shape
+    _check(load_library().rf_rope_rotate(_ptr(x), _ptr(out), B * H, N, D, float(base), int(pos_offset),
+                                         _DTYPE[x.dtype], _stream(x)))
+    return out
+
+
+def fwd_prerotated(q, k, v, rope_base, scale=None, mask="none", window=0, out=None, lse=None,
+                   alibi_slopes=None):
+    """RoPE attention as two passes: rotate q and k into temporaries, then the
+    fused forward without rotation (the other side of the Rotation Calculus)."""
+    qr = rope_rotate(q, rope_base, pos_offset=k.shape[2] - q.shape[2])
+    kr = rope_rotate(k, rope_base, pos_offset=0)
+    return fwd(qr, kr, v, scale=scale, mask=mask, window=window, rope_base=0.0, out=out, lse=lse,
+               alibi_slopes=alibi_slopes)
 
 
 def decode(q, k, v, num_splits=64, scale=None, mask="none", window=0, rope_base=0.0, alibi_slopes=None):

@@ -8,6 +8,7 @@
 
 #include "launch.hpp"
 #include "merge_kernel.hpp"
+#include "rope_kernel.hpp"
 
 namespace {
 
@@ -29,6 +30,14 @@ rf_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// theta_i / (2 pi) = base^(-2i/D) / (2 pi), i < D/2, in double on the host.
+rf::RopeTable rope_table(float base, int D) {
+    rf::RopeTable t{};
+    const double two_pi = 6.283185307179586476925;
+    for (int i = 0; i < D / 2 && i < 64; ++i) t.inv_period[i] = pow((double)base, -2.0 * i / D) / two_pi;
+    return t;
+}
 
 // Shared validation of the attention arguments.  Fills p on success.
 rf_status check_attn(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int Nq,
@@ -68,6 +77,7 @@ rf_status check_attn(const void* q, const void* k, const void* v, int B, int Hq,
     p.mask = mask_kind;
     p.window = mask_kind == RF_MASK_SLIDING ? window : 0;
     p.rope_base = rope_base > 0.f ? rope_base : 0.f;
+    if (p.rope_base > 0.f) p.rope = rope_table(p.rope_base, D);
     p.num_splits = 1;
     p.split_len = Nk;
     return RF_OK;
@@ -172,6 +182,31 @@ rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, floa
         return fail(RF_ERR_INVALID_ARG, "misaligned pointer (o_part 16 B, o 4 elements, lse 4 B)");
     return hip_status(rf::launch_merge(o_part, lse_part, o, lse, rows, num_splits, D, out_dtype, stream),
                       "rf_lse_merge launch");
+}
+
+rf_status rf_rope_rotate(const void* x, void* y, int rows, int N, int D, float base, int pos_offset, int dtype,
+                         hipStream_t stream) {
+    if (rows < 0 || N < 0) return fail(RF_ERR_INVALID_ARG, "negative size (rows=%d N=%d)", rows, N);
+    if (dtype != RF_F32 && dtype != RF_F16 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (!isfinite(base) || base <= 0.f) return fail(RF_ERR_INVALID_ARG, "base must be finite and > 0");
+    if (D != 64 && D != 128) return fail(RF_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+    const long long rows_n = (long long)rows * N;
+    if (rows_n == 0) return RF_OK;
+    if (!x || !y) return fail(RF_ERR_INVALID_ARG, "x or y is null");
+    if (!aligned16(x) || !aligned16(y)) return fail(RF_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if (pos_offset < 0 || (long long)pos_offset + N > 0x7fffffffLL) return fail(RF_ERR_INVALID_ARG, "positions out of range");
+    const int epc = dtype == RF_F32 ? 4 : 8;
+    const long long threads = rows_n * (D / 2 / epc);
+    if ((threads + rf::ROPE_THREADS - 1) / rf::ROPE_THREADS > 0x7fffffffLL) return fail(RF_ERR_INVALID_ARG, "too large");
+    dim3 grid((unsigned)((threads + rf::ROPE_THREADS - 1) / rf::ROPE_THREADS));
+    const rf::RopeTable table = rope_table(base, D);
+#define RF_ROPE_LAUNCH(TYPE, DD) \
+    hipLaunchKernelGGL((rf::rope_rotate_kernel<TYPE, DD>), grid, dim3(rf::ROPE_THREADS), 0, stream, (const TYPE*)x, (TYPE*)y, rows_n, N, table, pos_offset)
+    if (dtype == RF_F32) { if (D == 64) RF_ROPE_LAUNCH(float, 64); else RF_ROPE_LAUNCH(float, 128); }
+    else if (dtype == RF_F16) { if (D == 64) RF_ROPE_LAUNCH(_Float16, 64); else RF_ROPE_LAUNCH(_Float16, 128); }
+    else { if (D == 64) RF_ROPE_LAUNCH(__bf16, 64); else RF_ROPE_LAUNCH(__bf16, 128); }
+#undef RF_ROPE_LAUNCH
+    return hip_status(hipGetLastError(), "rf_rope_rotate launch");
 }
 
 const char* rf_status_string(rf_status s) {

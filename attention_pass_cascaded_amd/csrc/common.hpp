@@ -24,6 +24,12 @@ constexpr int FWD_WAVES = 4;
 constexpr int FWD_THREADS = 64 * FWD_WAVES;
 constexpr int FWD_BM = 32 * FWD_WAVES;  // query rows per work-group
 
+// theta_i / (2 pi) = base^(-2i/D) / (2 pi) for i < D/2, computed once on the
+// host in double precision and passed by value with the launch.
+struct RopeTable {
+    double inv_period[64];
+};
+
 // Everything a launch needs, filled and validated on the host.
 struct AttnParams {
     const void* q;
@@ -39,6 +45,7 @@ struct AttnParams {
     int window;
     float rope_base;   // > 0: RoPE on
     const float* alibi;  // [Hq] ALiBi slopes, or null
+    RopeTable rope;      // theta_i / (2 pi), filled on the host when RoPE is on
     int num_splits;    // 1 when not splitting
     int split_len;     // keys per chunk, ceil(Nk / num_splits)
     int split_mode;    // 1: write normalised partials + chunk lse
@@ -129,12 +136,6 @@ __device__ __forceinline__ void rope_cos_sin(double inv_period, int pos, float& 
     float rf = (float)r;
     c = __builtin_amdgcn_cosf(rf);
     s = __builtin_amdgcn_sinf(rf);
-}
-
-// theta_i / (2 pi) with theta_i = base^(-2 i / D).
-__device__ __forceinline__ double rope_inv_period(float base, int i, int D) {
-    const double inv_two_pi = 0.15915494309189533576888;
-    return exp2(-2.0 * (double)i / (double)D * log2((double)base)) * inv_two_pi;
 }
 
 }  // namespace rf

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(AttnParams p) 
     double ipd[ROPE ? EPL : 1];
     if (ROPE) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) ipd[e] = rope_inv_period(p.rope_base, (d0 + e) % (D / 2), D);
+        for (int e = 0; e < EPL; ++e) ipd[e] = p.rope.inv_period[(d0 + e) % (D / 2)];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll

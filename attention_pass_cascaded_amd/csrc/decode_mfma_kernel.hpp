@@ -108,7 +108,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float cs, sn;
-                    rope_cos_sin(rope_inv_period(p.rope_base, 32 * ks + 8 * q + i, D), my_pos, cs, sn);
+                    rope_cos_sin(p.rope.inv_period[32 * ks + 8 * q + i], my_pos, cs, sn);
                     const float x = qf[ks][i], y = qf[ks + NKS / 2][i];
                     qf[ks][i] = x * cs - y * sn;
                     qf[ks + NKS / 2][i] = x * sn + y * cs;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
 #pragma unroll
         for (int ks = 0; ks < NKS / 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ipd[8 * ks + i] = rope_inv_period(p.rope_base, 32 * ks + 8 * q + i, D);
+            for (int i = 0; i < 8; ++i) ipd[8 * ks + i] = p.rope.inv_period[32 * ks + 8 * q + i];
     }
 
     f32x4 oacc[NDB];

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
             for (int n = 0; n < QN / 2; ++n) {
                 const int d = F32 ? 2 * n + hi : 16 * (n / 8) + 8 * hi + (n % 8);
                 float cs, sn;
-                rope_cos_sin(rope_inv_period(p.rope_base, d, D), my_pos, cs, sn);
+                rope_cos_sin(p.rope.inv_period[d], my_pos, cs, sn);
                 const float x = qf[n], y = qf[n + QN / 2];
                 qf[n] = x * cs - y * sn;
                 qf[n + QN / 2] = x * sn + y * cs;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     if (ROPE) {
         const int cc = tid % (CPR / 2);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) ipd[e] = rope_inv_period(p.rope_base, cc * EPC + e, D);
+        for (int e = 0; e < EPC; ++e) ipd[e] = p.rope.inv_period[cc * EPC + e];
     }
 
     // ---------------- tile staging (global -> registers -> LDS)

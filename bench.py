@@ -213,6 +213,54 @@ def cpu_baseline(w, q, k, v, heads: int):
                       + f", {flops / 1e9:.2f} GFLOP in {dt:.1f} s, float64 numpy three-pass oracle"}
 
 
+def rotation_sweep(steps: int, warmup: int, Ns=(512, 1024, 2048, 4096, 8192, 16384)):
+    """Fused RoPE vs rotate-first, causal fp16 B=4 H=12 D=64 (AttnFuse Table 4's comparison).
+
+    speedup = (rotate q + rotate k + attention without RoPE) / (attention with fused RoPE);
+    above 1 the fused kernel wins.  N* is interpolated where the speedup crosses 1.
+    """
+    import torch
+    import attention_pass_cascaded_amd as rf
+    from workloads import gen_qkv
+    rows = []
+    for N in Ns:
+        q, k, v = gen_qkv(4, 12, 12, N, N, 64, "f16", seed=3, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((4, 12, N), dtype=torch.float32, device="cuda")
+        qr, kr = torch.empty_like(q), torch.empty_like(k)
+
+        def fused():
+            rf.fwd(q, k, v, scale=0.125, mask="causal", rope_base=10000.0, out=o, lse=lse)
+
+        def rotate_first():
+            rf.rope_rotate(q, 10000.0, 0, out=qr)
+            rf.rope_rotate(k, 10000.0, 0, out=kr)
+            rf.fwd(qr, kr, v, scale=0.125, mask="causal", out=o, lse=lse)
+
+        def plain():
+            rf.fwd(q, k, v, scale=0.125, mask="causal", out=o, lse=lse)
+
+        def rot_only():
+            rf.rope_rotate(q, 10000.0, 0, out=qr)
+            rf.rope_rotate(k, 10000.0, 0, out=kr)
+
+        t = {name: time_loop(fn, steps, warmup) for name, fn in
+             (("fused_ms", fused), ("rotate_first_ms", rotate_first), ("plain_causal_ms", plain),
+              ("rotate_qk_ms", rot_only))}
+        t["speedup_fused_over_rotate_first"] = t["rotate_first_ms"] / t["fused_ms"]
+        t["N"] = N
+        rows.append(t)
+        print(json.dumps(t), flush=True)
+    nstar = None
+    for a, b in zip(rows, rows[1:]):
+        sa, sb = a["speedup_fused_over_rotate_first"], b["speedup_fused_over_rotate_first"]
+        if (sa - 1) * (sb - 1) < 0:
+            la, lb = math.log(a["N"]), math.log(b["N"])
+            nstar = math.exp(la + (1 - sa) * (lb - la) / (sb - sa))
+    print(json.dumps({"rotation_calculus_crossover_N": nstar,
+                      "fused_wins_at": [r["N"] for r in rows if r["speedup_fused_over_rotate_first"] > 1]}))
+
+
 def copy_calibration(nbytes: int, steps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -233,6 +281,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads of batch 0 for the oracle (0: whole workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--rotation-sweep", action="store_true",
+                    help="fused RoPE vs rotate-first over N (prints one JSON line per N)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -248,6 +298,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.rotation_sweep:
+        rotation_sweep(args.steps, args.warmup)
         return
 
     if args.only:

@@ -139,6 +139,19 @@ size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits);
 rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                        int rows, int num_splits, int D, int out_dtype, hipStream_t stream);
 
+/*
+ * rf_rope_rotate — the rotary embedding alone, as a separate pass over HBM
+ * (the "pre-rotate" alternative of AttnFuse's Rotation Calculus: abstract,
+ * Table 4).  x, y: [rows, N, D] of dtype (rows = B*H), 16-byte aligned; y may
+ * equal x (in place).  Row n of every [N, D] slice is rotated to position
+ * pos_offset + n: pairs (x[i], x[i + D/2]), i < D/2, turn by
+ * (pos_offset + n) * base^(-2i/D), rounded once to dtype.  Use pos_offset =
+ * Nk - Nq for queries and 0 for keys to match rf_attn_fwd's positions.
+ * base > 0.  rows, N >= 0; D in {64, 128}.
+ */
+rf_status rf_rope_rotate(const void* x, void* y, int rows, int N, int D, float base, int pos_offset,
+                         int dtype, hipStream_t stream);
+
 /* rf_status_string — static text for a status code. */
 const char* rf_status_string(rf_status s);
 

@@ -214,3 +214,49 @@ def test_splitkv_alibi_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, S, mask, window
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q, k, v, scale, mask, window, rope, alibi_slopes=sl)
     compare(o, lse, ro, rl, TOL[dt], "alibi split")
+
+
+# ---------------------------------------------------------------- standalone RoPE (Rotation Calculus)
+@pytest.mark.parametrize("dt,D,N,pos", [("f16", 64, 77, 0), ("bf16", 128, 130, 1000), ("f32", 64, 33, 5),
+                                         ("f16", 128, 1, 32767)])
+def test_rope_rotate_matches_oracle(dt, D, N, pos):
+    g = torch.Generator().manual_seed(zlib.crc32(repr(("rope", dt, D, N, pos)).encode()))
+    x = torch.randn((2, 3, N, D), generator=g).to(DT[dt])
+    ref = oracle.rope_rotate(x, np.arange(N) + pos, 10000.0)          # fp64
+    y = rf.rope_rotate(x.cuda(), 10000.0, pos_offset=pos)
+    xi = x.cuda().clone()
+    rf.rope_rotate(xi, 10000.0, pos_offset=pos, out=xi)                 # in place
+    torch.cuda.synchronize()
+    got = y.float().cpu().double().numpy()
+    assert torch.equal(xi, y)
+    # one rounding of the exact rotation to the dtype, plus the fp32 angle/trig error
+    mant = {"f16": 10, "bf16": 7, "f32": 23}[dt]
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - mant)
+    err = np.abs(got - ref)
+    assert np.all(err <= ulp + 2e-4 * (1 + np.abs(ref))), float((err - ulp).max())
+
+
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("sliding", 100)])
+def test_prerotated_path_matches_oracle_and_fused(mask, window):
+    q, k, v = gen_qkv(1, 4, 4, 300, 300, 64, "f16", 21)
+    dev = torch.device("cuda")
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    o1, l1 = rf.fwd(qg, kg, vg, scale=0.125, mask=mask, window=window, rope_base=10000.0)
+    o2, l2 = rf.fwd_prerotated(qg, kg, vg, 10000.0, scale=0.125, mask=mask, window=window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, 0.125, mask, window, 10000.0)
+    compare(o2, l2, ro, rl, TOL["f16"], "prerotated")
+    # same fp16 rounding of the rotated operands on both sides: nearly identical
+    assert float((o1.float() - o2.float()).abs().max()) <= 2e-3
+
+
+def test_rope_mode_auto_switches_above_crossover():
+    from attention_pass_cascaded_amd._binding import ROPE_FUSED_MAX_N
+    N = ROPE_FUSED_MAX_N + 100
+    q, k, v = gen_qkv(1, 1, 1, 40, N, 64, "f16", 22)
+    dev = torch.device("cuda")
+    o, lse = rf.fwd(q.to(dev), k.to(dev), v.to(dev), scale=0.125, mask="causal", rope_base=10000.0,
+                    rope_mode="auto")
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, 0.125, "causal", rope_base=10000.0)
+    compare(o, lse, ro, rl, TOL["f16"], "auto rope")
