@@ -12,9 +12,13 @@ Contents
                 and the log-sum-exp merge, RoPE.  numpy, float64.
   brute.py      pure-Python scalar reference for tiny inputs (math.exp,
                 math.fsum), written from the textbook softmax definition.
+  backward.py   gradients dq, dk, dv of the forward by the chain rule
+                (softmax Jacobian row term, inverse RoPE rotation, GQA sums).
 
-Every function is pinned by ``tests/test_oracle.py`` (brute force, closed
-forms, invariants and a library routine the definition reduces to).
+Every function is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_backward.py`` (brute force, finite differences of the
+brute force, closed forms, invariants and library routines the definition
+reduces to).
 """
 from .cascade import (  # noqa: F401
     attention,
@@ -27,3 +31,4 @@ from .cascade import (  # noqa: F401
     visible_mask,
     softmax_probs,
 )
+from .backward import attention_backward, row_terms  # noqa: F401
