@@ -2,13 +2,14 @@
 
 The product is the C-ABI library ``librfattn.so`` (``include/rf_attn.h``),
 built from the HIP sources in ``csrc/``.  This package is its thin Python
-binding: ``fwd``, ``splitkv_fwd``, ``lse_merge`` and ``decode`` marshal torch
+binding: ``fwd``, ``bwd``, ``splitkv_fwd``, ``lse_merge``, ``decode`` and ``rope_rotate`` marshal torch
 tensors (device memory and the current stream) into the C calls.
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     RFError,
+    bwd,
     decode,
     fwd,
     fwd_prerotated,
@@ -19,5 +20,5 @@ from ._binding import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["fwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "workspace_bytes", "load_library",
+__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "workspace_bytes", "load_library",
            "RFError", "LIB_PATH", "EXPORTED"]

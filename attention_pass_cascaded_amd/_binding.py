@@ -22,8 +22,8 @@ _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
 EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
-            "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_status_string",
-            "rf_last_error")
+            "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_attn_bwd",
+            "rf_attn_bwd_workspace_bytes", "rf_status_string", "rf_last_error")
 
 
 class RFError(RuntimeError):
@@ -59,6 +59,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_lse_merge.restype = i
     lib.rf_rope_rotate.argtypes = [vp, vp, i, i, i, f, i, i, vp]
     lib.rf_rope_rotate.restype = i
+    lib.rf_attn_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, i, f, i, i, f, vp, i, vp]
+    lib.rf_attn_bwd.restype = i
+    lib.rf_attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.rf_attn_bwd_workspace_bytes.restype = sz
     lib.rf_status_string.argtypes = [i]
     lib.rf_status_string.restype = ctypes.c_char_p
     lib.rf_last_error.argtypes = []
@@ -215,3 +219,27 @@ def decode(q, k, v, num_splits=64, scale=None, mask="none", window=0, rope_base=
     """Split-KV attention: partials then log-sum-exp merge.  Returns (o, lse) like fwd."""
     op, lp = splitkv_fwd(q, k, v, num_splits, scale, mask, window, rope_base, alibi_slopes=alibi_slopes)
     return lse_merge(op, lp, out_dtype=q.dtype)
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, mask="none", window=0, rope_base=0.0, alibi_slopes=None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of fwd for the loss gradient dout, from the
+    forward's o and lse (same arguments as the forward call)."""
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
+        if not t.is_cuda or t.dtype != q.dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    lib = load_library()
+    if workspace is None:
+        nbytes = int(lib.rf_attn_bwd_workspace_bytes(B, Hq, Nq))
+        workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    slopes = _slopes(alibi_slopes, Hq, q.device)
+    _check(lib.rf_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                           _ptr(dv), _ptr(workspace), B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask],
+                           int(window), float(rope_base), _ptr(slopes), _DTYPE[q.dtype], _stream(q)))
+    return dq, dk, dv

@@ -6,6 +6,7 @@
 
 #include <string>
 
+#include "bwd_kernel.hpp"
 #include "launch.hpp"
 #include "merge_kernel.hpp"
 #include "rope_kernel.hpp"
@@ -207,6 +208,59 @@ rf_status rf_rope_rotate(const void* x, void* y, int rows, int N, int D, float b
     else { if (D == 64) RF_ROPE_LAUNCH(__bf16, 64); else RF_ROPE_LAUNCH(__bf16, 128); }
 #undef RF_ROPE_LAUNCH
     return hip_status(hipGetLastError(), "rf_rope_rotate launch");
+}
+
+size_t rf_attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+    if (B < 0 || Hq < 1 || Nq < 0) return 0;
+    return (size_t)B * Hq * Nq * sizeof(float);
+}
+
+rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int D, float scale, int mask_kind, int window, float rope_base,
+                      const float* alibi_slopes, int dtype, hipStream_t stream) {
+    rf::AttnParams a;
+    rf_status st = check_attn(q, k, v, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base, dtype, a);
+    if (st != RF_OK) return st;
+    if (dtype == RF_F32) return fail(RF_ERR_UNSUPPORTED, "rf_attn_bwd supports float16 and bfloat16 inputs");
+    if (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) return fail(RF_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+    const bool q_nonempty = (size_t)B * Nq > 0;
+    const bool kv_nonempty = (size_t)B * Nk > 0;
+    if (q_nonempty && (!o || !lse || !dout || !dq || !workspace))
+        return fail(RF_ERR_INVALID_ARG, "o, lse, dout, dq and workspace are required");
+    if (kv_nonempty && (!dk || !dv)) return fail(RF_ERR_INVALID_ARG, "dk and dv are required");
+    if ((o && !aligned16(o)) || (dout && !aligned16(dout)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
+        (dv && !aligned16(dv)) || (lse && ((uintptr_t)lse & 3u)) || (workspace && ((uintptr_t)workspace & 3u)))
+        return fail(RF_ERR_INVALID_ARG, "o, dout, dq, dk, dv must be 16-byte aligned, lse and workspace 4-byte aligned");
+    if ((size_t)B * Hq * ((Nq + rf::FWD_BM - 1) / rf::FWD_BM) > 0x7fffffffu ||
+        (size_t)B * Hkv * ((Nk + rf::BWD_BK - 1) / rf::BWD_BK) > 0x7fffffffu)
+        return fail(RF_ERR_INVALID_ARG, "grid too large");
+    if (!q_nonempty && !kv_nonempty) return RF_OK;
+    rf::BwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.drow = workspace;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.D = D;
+    p.scale = scale;
+    p.mask = a.mask;
+    p.window = a.window;
+    p.rope_base = a.rope_base;
+    p.alibi = alibi_slopes;
+    p.rope = a.rope;
+    const hipError_t e = dtype == RF_F16 ? rf::launch_bwd_f16(p, stream) : rf::launch_bwd_bf16(p, stream);
+    return hip_status(e, "rf_attn_bwd launch");
 }
 
 const char* rf_status_string(rf_status s) {

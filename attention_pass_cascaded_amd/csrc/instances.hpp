@@ -1,6 +1,7 @@
 // Template instantiation and dispatch on (D, RoPE, rows) for one dtype.
 #pragma once
 
+#include "bwd_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "decode_mfma_kernel.hpp"
 #include "fwd_kernel.hpp"
@@ -73,7 +74,49 @@ hipError_t dec_dispatch(const AttnParams& p, hipStream_t s) {
         return p.D == 64 ? dec_launch_d<T, 64>(p, s) : dec_launch_d<T, 128>(p, s);
 }
 
+// Backward: row terms, then the key-parallel dk/dv kernel and the
+// query-parallel dq kernel (independent of each other).
+template <typename T, int D, bool ROPE, bool ALIBI>
+hipError_t bwd_launch_one(const BwdParams& p, hipStream_t s) {
+    const long long rows = (long long)p.B * p.Hq * p.Nq;
+    if (rows > 0) {
+        const long long threads = rows * (D / 8);
+        hipLaunchKernelGGL((bwd_rowterm_kernel<T, D>), dim3((unsigned)((threads + BWD_THREADS - 1) / BWD_THREADS)),
+                           dim3(BWD_THREADS), 0, s, (const T*)p.o, (const T*)p.dout, p.drow, rows);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if ((long long)p.B * p.Nk > 0) {
+        dim3 grid((unsigned)(p.B * p.Hkv * ((p.Nk + BWD_BK - 1) / BWD_BK)));
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, ROPE, ALIBI>), grid, dim3(BWD_THREADS), 0, s, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (rows > 0) {
+        dim3 grid((unsigned)(p.B * p.Hq * ((p.Nq + FWD_BM - 1) / FWD_BM)));
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, ROPE, ALIBI>), grid, dim3(FWD_THREADS), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_dispatch_d(const BwdParams& p, hipStream_t s) {
+    const bool rope = p.rope_base > 0.f;
+    if (p.alibi) return rope ? bwd_launch_one<T, D, true, true>(p, s) : bwd_launch_one<T, D, false, true>(p, s);
+    return rope ? bwd_launch_one<T, D, true, false>(p, s) : bwd_launch_one<T, D, false, false>(p, s);
+}
+
+template <typename T>
+hipError_t bwd_dispatch(const BwdParams& p, hipStream_t s) {
+    return p.D == 64 ? bwd_dispatch_d<T, 64>(p, s) : bwd_dispatch_d<T, 128>(p, s);
+}
+
 }  // namespace rf
+
+#define RF_DEFINE_BWD_LAUNCHERS(SUFFIX, TYPE)                                                      \
+    namespace rf {                                                                                 \
+    hipError_t launch_bwd_##SUFFIX(const BwdParams& p, hipStream_t s) { return bwd_dispatch<TYPE>(p, s); } \
+    }
 
 #define RF_DEFINE_LAUNCHERS(SUFFIX, TYPE)                                                          \
     namespace rf {                                                                                 \

@@ -18,6 +18,11 @@ hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_decode_f16(const AttnParams& p, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);
 
+// Backward (16-bit inputs): row terms, dk/dv and dq kernels.
+struct BwdParams;
+hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
+
 hipError_t launch_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                         int rows, int S, int D, int dtype, hipStream_t s);
 

@@ -152,6 +152,39 @@ rf_status rf_lse_merge(const float* o_part, const float* lse_part, void* o, floa
 rf_status rf_rope_rotate(const void* x, void* y, int rows, int N, int D, float base, int pos_offset,
                          int dtype, hipStream_t stream);
 
+/*
+ * rf_attn_bwd — gradients of rf_attn_fwd (the backward of a training step:
+ * AttnFuse abstract and Table 9, forward + backward + optimiser step).  The
+ * pages print no backward formulas; this is the chain rule through the
+ * forward's definition, with P recomputed from the saved lse:
+ *   P_ij = exp(s_ij - lse_i),   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,
+ *   D_i = dO_i . o_i,           dS_ij = P_ij (dP_ij - D_i),
+ *   dq_i = R(p_i)^T scale sum_j dS_ij k'_j,   dk_j = R(j)^T scale sum_i dS_ij q'_i
+ * (R = the RoPE rotation; ALiBi adds an input-independent bias, its slopes get
+ * no gradient).  With GQA, dk and dv sum over the Hq/Hkv query heads of the
+ * group.  lse is taken as not feeding the loss (its gradient is zero).
+ *
+ * q, k, v, o, lse: the forward's inputs and outputs (same mask, window,
+ * rope_base, scale and slopes as the forward call).  dout: gradient of the
+ * loss with respect to o, layout of o.  dq [B, Hq, Nq, D], dk and dv
+ * [B, Hkv, Nk, D]: outputs of `dtype`, every element written (keys no query
+ * sees get 0).  workspace: device float32 buffer of at least
+ * rf_attn_bwd_workspace_bytes(B, Hq, Nq) bytes, 4-byte aligned, overwritten.
+ * dtype: RF_F16 or RF_BF16 (RF_F32 returns RF_ERR_UNSUPPORTED).  P and dS
+ * are rounded to dtype for the matrix products, accumulation is float32,
+ * each output is rounded once.  Deterministic: no atomics.
+ * Errors as the forward, plus RF_ERR_INVALID_ARG for a missing output or
+ * workspace.
+ */
+rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* workspace,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                      float scale, int mask_kind, int window, float rope_base,
+                      const float* alibi_slopes, int dtype, hipStream_t stream);
+
+/* rf_attn_bwd_workspace_bytes — B*Hq*Nq*4 (the per-row D_i); 0 for invalid sizes. */
+size_t rf_attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
 /* rf_status_string — static text for a status code. */
 const char* rf_status_string(rf_status s);
 

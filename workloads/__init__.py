@@ -101,6 +101,14 @@ def gen_qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed, device="cpu"):
     return q, k, v
 
 
+def gen_grad_out(shape, dtype, seed, device="cpu"):
+    """dO for a backward: N(0,1) float32 from its own generator, cast to ``dtype``."""
+    if isinstance(dtype, str):
+        dtype = _DT[dtype]
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    return gen_normal(shape, dtype, g)
+
+
 def alibi_slopes(H: int):
     """The usual geometric ALiBi slope schedule 2^(-8h/H), h = 1..H (a fixed input)."""
     return [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
