@@ -145,6 +145,35 @@ def run_prefill(w, steps, warmup):
     return res, (q, k, v)
 
 
+def run_backward(w, steps, warmup):
+    """rf_attn_bwd (row terms + dk/dv + dq kernels) on a prefill workload, with
+    o and lse from the fused forward.  Algorithmic flops: 5 products of 2*D
+    flops per visible pair (S recomputed, dP, dV, dK, dQ) = 2.5x the forward;
+    the kernels execute 7 (S and dP are recomputed in both the dk/dv and the
+    dq kernel), reported as executed_TFLOP/s."""
+    import torch
+    import attention_pass_cascaded_amd as rf
+    from workloads import gen_grad_out, gen_workload
+    q, k, v = gen_workload(w, device="cuda")
+    do = gen_grad_out(q.shape, w.dtype, w.seed + 100, device="cuda")
+    o, lse = rf.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, rope_base=w.rope_base)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(w.B * w.Hq * w.Nq, dtype=torch.float32, device="cuda")
+
+    def step():
+        rf.bwd(q, k, v, o, lse, do, scale=w.scale, mask=w.mask, window=w.window, rope_base=w.rope_base,
+               dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms = time_loop(step, steps, warmup)
+    flops = 2.5 * alg_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {"workload": w.name, "ms": ms, "TFLOP/s": tflops, "executed_TFLOP/s": tflops * 7.0 / 5.0,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                         "frac": tflops / peak, "traffic": None},
+            "alg_gflop": flops / 1e9}
+
+
 def run_decode(w, steps, warmup):
     import torch
     import attention_pass_cascaded_amd as rf
@@ -278,6 +307,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default=None, help="time a single workload (for profiling runs)")
+    ap.add_argument("--only-bwd", default=None, metavar="WORKLOAD", help="time the backward of one prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads of batch 0 for the oracle (0: whole workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -303,6 +333,9 @@ def main():
         rotation_sweep(args.steps, args.warmup)
         return
 
+    if args.only_bwd:
+        print(json.dumps(run_backward(by_name(args.only_bwd), args.steps, args.warmup)), flush=True)
+        return
     if args.only:
         w = by_name(args.only)
         res = run_decode(w, args.steps, args.warmup) if w.num_splits else run_prefill(w, args.steps, args.warmup)[0]
@@ -320,6 +353,8 @@ def main():
         variants[name] = {"ms": r["ms"], "TFLOP/s": r["TFLOP/s"], "GB/s": r["GB/s"],
                           "mfma_frac": r["roofline"]["frac"], "hbm_frac": r["hbm_frac"]}
         print(f"# {name}: {r['ms']:.4f} ms", file=sys.stderr, flush=True)
+    bwd = run_backward(w, max(1, args.steps // 4), max(1, args.warmup // 4))
+    print(f"# backward {w.name}: {bwd['ms']:.4f} ms, {bwd['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
 
     line = {
@@ -333,6 +368,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": dec,
         "variants": variants,
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
 
