@@ -14,9 +14,11 @@ Contents
                 math.fsum), written from the textbook softmax definition.
   backward.py   gradients dq, dk, dv of the forward by the chain rule
                 (softmax Jacobian row term, inverse RoPE rotation, GQA sums).
+  layernorm.py  a second cascaded reduction: LayerNorm mean -> variance ->
+                normalise, three-pass and incremental (n, mean, M2) forms.
 
-Every function is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_backward.py`` (brute force, finite differences of the
+Every function is pinned by ``tests/test_oracle.py``,
+``tests/test_oracle_backward.py`` and ``tests/test_oracle_layernorm.py`` (brute force, finite differences of the
 brute force, closed forms, invariants and library routines the definition
 reduces to).
 """
@@ -32,3 +34,4 @@ from .cascade import (  # noqa: F401
     softmax_probs,
 )
 from .backward import attention_backward, row_terms  # noqa: F401
+from .layernorm import layer_norm, layer_norm_incremental  # noqa: F401
