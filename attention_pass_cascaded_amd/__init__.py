@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     decode,
     fwd,
     fwd_prerotated,
+    layernorm,
     rope_rotate,
     load_library,
     lse_merge,
@@ -20,5 +21,5 @@ from ._binding import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "workspace_bytes", "load_library",
+__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "workspace_bytes", "load_library",
            "RFError", "LIB_PATH", "EXPORTED"]

@@ -23,7 +23,7 @@ _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
 EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
             "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_attn_bwd",
-            "rf_attn_bwd_workspace_bytes", "rf_status_string", "rf_last_error")
+            "rf_attn_bwd_workspace_bytes", "rf_layernorm_fwd", "rf_status_string", "rf_last_error")
 
 
 class RFError(RuntimeError):
@@ -63,6 +63,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_attn_bwd.restype = i
     lib.rf_attn_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.rf_attn_bwd_workspace_bytes.restype = sz
+    lib.rf_layernorm_fwd.argtypes = [vp] * 6 + [i, i, f, i, vp]
+    lib.rf_layernorm_fwd.restype = i
     lib.rf_status_string.argtypes = [i]
     lib.rf_status_string.restype = ctypes.c_char_p
     lib.rf_last_error.argtypes = []
@@ -243,3 +245,20 @@ def bwd(q, k, v, o, lse, dout, scale=None, mask="none", window=0, rope_base=0.0,
                            _ptr(dv), _ptr(workspace), B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask],
                            int(window), float(rope_base), _ptr(slopes), _DTYPE[q.dtype], _stream(q)))
     return dq, dk, dv
+
+
+def layernorm(x, gamma, beta, eps=1e-5, y=None, mean=None, rstd=None):
+    """LayerNorm over the last axis of x [..., H].  Returns (y, mean, rstd)."""
+    if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPE:
+        raise ValueError("x must be a contiguous GPU tensor of float32/float16/bfloat16")
+    H = x.shape[-1]
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if not t.is_cuda or t.dtype != x.dtype or tuple(t.shape) != (H,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [H] GPU tensor of x's dtype")
+    rows = x.numel() // H if H else 0
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _check(load_library().rf_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd),
+                                           rows, H, float(eps), _DTYPE[x.dtype], _stream(x)))
+    return y, mean, rstd

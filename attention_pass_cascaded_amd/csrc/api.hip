@@ -8,6 +8,7 @@
 
 #include "bwd_kernel.hpp"
 #include "launch.hpp"
+#include "layernorm_kernel.hpp"
 #include "merge_kernel.hpp"
 #include "rope_kernel.hpp"
 
@@ -261,6 +262,38 @@ rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o
     p.rope = a.rope;
     const hipError_t e = dtype == RF_F16 ? rf::launch_bwd_f16(p, stream) : rf::launch_bwd_bf16(p, stream);
     return hip_status(e, "rf_attn_bwd launch");
+}
+
+rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                           int rows, int H, float eps, int dtype, hipStream_t stream) {
+    if (rows < 0 || H < 1) return fail(RF_ERR_INVALID_ARG, "rows must be >= 0 and H >= 1 (rows=%d H=%d)", rows, H);
+    if (dtype != RF_F32 && dtype != RF_F16 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (!isfinite(eps) || eps < 0.f) return fail(RF_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const int epc = dtype == RF_F32 ? 4 : 8;
+    if (H % epc) return fail(RF_ERR_UNSUPPORTED, "H must be a multiple of %d for this dtype (got %d)", epc, H);
+    const int nch = (H / epc + rf::LN_THREADS - 1) / rf::LN_THREADS;
+    if (nch > rf::LN_MAX_CHUNKS)
+        return fail(RF_ERR_UNSUPPORTED, "H = %d too large (at most %d for this dtype)", H, rf::LN_THREADS * rf::LN_MAX_CHUNKS * epc);
+    if (rows == 0) return RF_OK;
+    if (!x || !gamma || !beta || !y || !mean || !rstd) return fail(RF_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(y) || ((uintptr_t)mean & 3u) ||
+        ((uintptr_t)rstd & 3u))
+        return fail(RF_ERR_INVALID_ARG, "x, gamma, beta, y must be 16-byte aligned, mean and rstd 4-byte aligned");
+    dim3 grid((unsigned)rows);
+#define RF_LN(TYPE, N)                                                                                    \
+    hipLaunchKernelGGL((rf::layernorm_kernel<TYPE, N>), grid, dim3(rf::LN_THREADS), 0, stream, (const TYPE*)x, \
+                       (const TYPE*)gamma, (const TYPE*)beta, (TYPE*)y, mean, rstd, H, eps)
+#define RF_LN_T(TYPE)                           \
+    if (nch <= 1) RF_LN(TYPE, 1);               \
+    else if (nch <= 2) RF_LN(TYPE, 2);          \
+    else if (nch <= 4) RF_LN(TYPE, 4);          \
+    else RF_LN(TYPE, 8)
+    if (dtype == RF_F32) { RF_LN_T(float); }
+    else if (dtype == RF_F16) { RF_LN_T(_Float16); }
+    else { RF_LN_T(__bf16); }
+#undef RF_LN_T
+#undef RF_LN
+    return hip_status(hipGetLastError(), "rf_layernorm_fwd launch");
 }
 
 const char* rf_status_string(rf_status s) {

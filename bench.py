@@ -174,6 +174,30 @@ def run_backward(w, steps, warmup):
             "alg_gflop": flops / 1e9}
 
 
+def run_layernorm(steps, warmup):
+    """rf_layernorm_fwd on the LayerNorm workload: HBM-bound (x read once, y
+    written once; gamma, beta, mean and rstd are counted too)."""
+    import torch
+    import attention_pass_cascaded_amd as rf
+    from workloads import LN_WORKLOAD as w, gen_layernorm
+    x, g, b = gen_layernorm(w["rows"], w["H"], w["dtype"], w["seed"], device="cuda")
+    y = torch.empty_like(x)
+    mean = torch.empty(w["rows"], dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+
+    def step():
+        rf.layernorm(x, g, b, w["eps"], y=y, mean=mean, rstd=rstd)
+
+    ms = time_loop(step, steps, warmup)
+    es = x.element_size()
+    byts = 2 * w["rows"] * w["H"] * es + 2 * w["H"] * es + 8 * w["rows"]
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": w["name"], "ms": ms, "GB/s": gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+            "alg_mb": byts / 1e6}
+
+
 def run_decode(w, steps, warmup):
     import torch
     import attention_pass_cascaded_amd as rf
@@ -308,6 +332,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default=None, help="time a single workload (for profiling runs)")
     ap.add_argument("--only-bwd", default=None, metavar="WORKLOAD", help="time the backward of one prefill workload")
+    ap.add_argument("--only-layernorm", action="store_true", help="time the LayerNorm workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads of batch 0 for the oracle (0: whole workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -333,6 +358,9 @@ def main():
         rotation_sweep(args.steps, args.warmup)
         return
 
+    if args.only_layernorm:
+        print(json.dumps(run_layernorm(args.steps, args.warmup)), flush=True)
+        return
     if args.only_bwd:
         print(json.dumps(run_backward(by_name(args.only_bwd), args.steps, args.warmup)), flush=True)
         return
@@ -355,6 +383,8 @@ def main():
         print(f"# {name}: {r['ms']:.4f} ms", file=sys.stderr, flush=True)
     bwd = run_backward(w, max(1, args.steps // 4), max(1, args.warmup // 4))
     print(f"# backward {w.name}: {bwd['ms']:.4f} ms, {bwd['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    ln = run_layernorm(args.steps, args.warmup)
+    print(f"# layernorm {ln['workload']}: {ln['ms']:.4f} ms, {ln['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
 
     line = {
@@ -369,6 +399,7 @@ def main():
         "decode": dec,
         "variants": variants,
         "backward": bwd,
+        "layernorm": ln,
     }
     print(json.dumps(line), flush=True)
 

@@ -185,6 +185,28 @@ rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o
 /* rf_attn_bwd_workspace_bytes — B*Hq*Nq*4 (the per-row D_i); 0 for invalid sizes. */
 size_t rf_attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 
+/*
+ * rf_layernorm_fwd — LayerNorm, a second cascaded reduction run through the
+ * same incremental machinery (RedFuser abstract and Table 1: a later
+ * reduction that reads an earlier one's result; "Operator Fusion" guide,
+ * section 2, Pattern 2: mean, then variance around it, then normalise):
+ *   mean_r = sum_h x[r,h] / H,   var_r = sum_h (x[r,h] - mean_r)^2 / H,
+ *   rstd_r = 1 / sqrt(var_r + eps),
+ *   y[r,h] = (x[r,h] - mean_r) * rstd_r * gamma[h] + beta[h].
+ * Each row is read from HBM once: a running (n, mean, M2) per lane is
+ * updated chunk by chunk (a chunk that moves the mean by delta adds
+ * delta^2 n_a n_b / n to M2), merged across the work-group, then the row is
+ * normalised from registers.
+ * x, y: [rows, H] of dtype, 16-byte aligned (y must not alias x); gamma,
+ * beta: [H] of dtype, 16-byte aligned; mean, rstd: float32 [rows] outputs.
+ * Statistics in float32, y rounded once to dtype.  rows >= 0, eps >= 0;
+ * H a multiple of 8 (float16/bfloat16) or 4 (float32), at most 16384
+ * (16-bit) or 8192 (float32), else RF_ERR_UNSUPPORTED.
+ */
+rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y,
+                           float* mean, float* rstd, int rows, int H, float eps,
+                           int dtype, hipStream_t stream);
+
 /* rf_status_string — static text for a status code. */
 const char* rf_status_string(rf_status s);
 

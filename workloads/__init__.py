@@ -26,7 +26,8 @@ import math
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal", "alibi_slopes"]
+__all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal", "alibi_slopes", "gen_grad_out",
+           "LN_WORKLOAD", "gen_layernorm"]
 
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -118,3 +119,24 @@ def gen_workload(w: Workload, seed: int | None = None, device="cpu"):
     return gen_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, w.torch_dtype,
                    w.seed if seed is None else seed, device=device)
 
+
+# LayerNorm (the second cascaded reduction): the pages' workload tables for
+# it are missing, so the shape is chosen: the hidden states of the Llama-3-8B
+# step of AttnFuse Table 9 (width 4096) for B=4 sequences of 4096 tokens.
+LN_WORKLOAD = dict(name="layernorm_bf16_r16384_h4096", rows=16384, H=4096, dtype="bf16", eps=1e-5, seed=6)
+
+
+def gen_layernorm(rows, H, dtype, seed, device="cpu"):
+    """(x [rows, H], gamma [H], beta [H]).  Rows get their own offset in
+    [-8, 8) and spread in [0.5, 2) (so the mean is large next to the spread,
+    the case a one-pass sum of squares gets wrong); gamma = 1 + 0.1 N(0,1),
+    beta = 0.1 N(0,1).  Draw order: x noise, offsets, spreads, gamma, beta."""
+    if isinstance(dtype, str):
+        dtype = _DT[dtype]
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    z = torch.randn((rows, H), generator=g, dtype=torch.float32, device=device)
+    off = torch.rand((rows, 1), generator=g, dtype=torch.float32, device=device) * 16.0 - 8.0
+    spread = torch.rand((rows, 1), generator=g, dtype=torch.float32, device=device) * 1.5 + 0.5
+    gamma = 1.0 + 0.1 * torch.randn((H,), generator=g, dtype=torch.float32, device=device)
+    beta = 0.1 * torch.randn((H,), generator=g, dtype=torch.float32, device=device)
+    return (z * spread + off).to(dtype), gamma.to(dtype), beta.to(dtype)
