@@ -44,6 +44,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "fwd": ["attention_pass_cascaded_amd/csrc/fwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "decode": ["attention_pass_cascaded_amd/csrc/decode_mfma_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "layernorm": ["attention_pass_cascaded_amd/csrc/layernorm_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
 }
 
 
@@ -194,7 +195,7 @@ def run_layernorm(steps, warmup):
     gbs = byts / (ms * 1e-3) / 1e9
     return {"workload": w["name"], "ms": ms, "GB/s": gbs,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_from_profiles("layernorm", w["name"])},
             "alg_mb": byts / 1e6}
 
 
