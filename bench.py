@@ -326,6 +326,16 @@ def copy_calibration(nbytes: int, steps: int):
     print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": steps}))
 
 
+def copy_rate(nbytes: int = 1 << 30, steps: int = 20) -> float:
+    """GB/s (read + write) of a plain device copy: the HBM rate a streaming
+    kernel can practically reach on this machine, reported next to the 8 TB/s peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = time_loop(lambda: dst.copy_(src), steps, 3)
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +396,8 @@ def main():
     print(f"# backward {w.name}: {bwd['ms']:.4f} ms, {bwd['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     ln = run_layernorm(args.steps, args.warmup)
     print(f"# layernorm {ln['workload']}: {ln['ms']:.4f} ms, {ln['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
+    copy_gbs = copy_rate()
+    print(f"# device copy: {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
 
     line = {
@@ -401,6 +413,7 @@ def main():
         "variants": variants,
         "backward": bwd,
         "layernorm": ln,
+        "hbm_copy_GB/s": copy_gbs,
     }
     print(json.dumps(line), flush=True)
 
