@@ -289,6 +289,7 @@ __global__ __launch_bounds__(FWD_THREADS, D == 64 ? 2 : 1) void attn_bwd_dq_kern
                 }
             }
             if (need_mask) {
+                // visible iff rel_lo <= offset <= rel_hi; & keeps it branch-free
                 const int rel_hi = lim_hi - k0 - 4 * hi;
                 const int rel_lo = lim_lo - k0 - 4 * hi;
 #pragma unroll
@@ -296,8 +297,7 @@ __global__ __launch_bounds__(FWD_THREADS, D == 64 ? 2 : 1) void attn_bwd_dq_kern
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int off = 32 * kb + 8 * (j / 4) + (j % 4);
-                        const bool vis = p.mask == RF_MASK_SLIDING ? (off <= rel_hi && off >= rel_lo) : off <= rel_hi;
-                        sacc[kb][j] = vis ? sacc[kb][j] : -INFINITY;
+                        sacc[kb][j] = ((off <= rel_hi) & (off >= rel_lo)) ? sacc[kb][j] : -INFINITY;
                     }
             }
             if constexpr (ALIBI) {
@@ -613,15 +613,18 @@ __global__ __launch_bounds__(BWD_THREADS, D == 64 ? 2 : 1) void attn_bwd_dkdv_ke
             const int rel = my_key - pos_off - q0 - 4 * hi;  // causal: visible iff off >= rel
             const int rows_left = p.Nq - q0 - 4 * hi;        // valid iff off < rows_left
             if (need_mask) {
+                // visible iff lo_b <= offset <= hi_b (bounds per lane; & keeps
+                // every element branch-free)
+                const int lo_b = p.mask != RF_MASK_NONE ? rel : -(1 << 30);
+                int hi_b = rows_left - 1;
+                if (p.mask == RF_MASK_SLIDING) hi_b = min(hi_b, rel + p.window - 1);
+                if (!key_ok) hi_b = -1;
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int off = 32 * qb + 8 * (j / 4) + (j % 4);
-                        bool vis = key_ok && off < rows_left;
-                        if (p.mask != RF_MASK_NONE) vis = vis && off >= rel;
-                        if (p.mask == RF_MASK_SLIDING) vis = vis && off < rel + p.window;
-                        sacc[qb][j] = vis ? sacc[qb][j] : -INFINITY;
+                        sacc[qb][j] = ((off >= lo_b) & (off <= hi_b)) ? sacc[qb][j] : -INFINITY;
                     }
             }
             if constexpr (ALIBI) {

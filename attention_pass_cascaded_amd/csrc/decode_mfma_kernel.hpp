@@ -216,7 +216,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
                 const int off = 16 * kgp + i;
                 float sv = sacc[kgp][i];
                 if constexpr (ALIBI) sv = fmaf(sv, c, -slope2 * fabsf(kd + (float)off));
-                sacc[kgp][i] = (off <= rel_hi && off >= rel_lo) ? sv : -INFINITY;
+                sacc[kgp][i] = ((off <= rel_hi) & (off >= rel_lo)) ? sv : -INFINITY;
                 mx = fmaxf(mx, sacc[kgp][i]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
