@@ -16,9 +16,12 @@ Contents
                 (softmax Jacobian row term, inverse RoPE rotation, GQA sums).
   layernorm.py  a second cascaded reduction: LayerNorm mean -> variance ->
                 normalise, three-pass and incremental (n, mean, M2) forms.
+  topk.py       softmax followed by TopK (the max/+ row of RedFuser Table 1),
+                three-pass and incremental (m, l, k best) forms.
 
 Every function is pinned by ``tests/test_oracle.py``,
-``tests/test_oracle_backward.py`` and ``tests/test_oracle_layernorm.py`` (brute force, finite differences of the
+``tests/test_oracle_backward.py``, ``tests/test_oracle_layernorm.py`` and
+``tests/test_oracle_topk.py`` (brute force, finite differences of the
 brute force, closed forms, invariants and library routines the definition
 reduces to).
 """
@@ -35,3 +38,4 @@ from .cascade import (  # noqa: F401
 )
 from .backward import attention_backward, row_terms  # noqa: F401
 from .layernorm import layer_norm, layer_norm_incremental  # noqa: F401
+from .topk import softmax_topk, softmax_topk_incremental  # noqa: F401
