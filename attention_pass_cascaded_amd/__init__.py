@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     fwd,
     fwd_prerotated,
     layernorm,
+    softmax_topk,
     rope_rotate,
     load_library,
     lse_merge,
@@ -21,5 +22,5 @@ from ._binding import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "workspace_bytes", "load_library",
+__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "softmax_topk", "workspace_bytes", "load_library",
            "RFError", "LIB_PATH", "EXPORTED"]

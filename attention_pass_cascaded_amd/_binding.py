@@ -23,7 +23,8 @@ _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
 EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
             "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_attn_bwd",
-            "rf_attn_bwd_workspace_bytes", "rf_layernorm_fwd", "rf_status_string", "rf_last_error")
+            "rf_attn_bwd_workspace_bytes", "rf_layernorm_fwd", "rf_softmax_topk", "rf_status_string",
+            "rf_last_error")
 
 
 class RFError(RuntimeError):
@@ -65,6 +66,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_attn_bwd_workspace_bytes.restype = sz
     lib.rf_layernorm_fwd.argtypes = [vp] * 6 + [i, i, f, i, vp]
     lib.rf_layernorm_fwd.restype = i
+    lib.rf_softmax_topk.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.rf_softmax_topk.restype = i
     lib.rf_status_string.argtypes = [i]
     lib.rf_status_string.restype = ctypes.c_char_p
     lib.rf_last_error.argtypes = []
@@ -262,3 +265,18 @@ def layernorm(x, gamma, beta, eps=1e-5, y=None, mean=None, rstd=None):
     _check(load_library().rf_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd),
                                            rows, H, float(eps), _DTYPE[x.dtype], _stream(x)))
     return y, mean, rstd
+
+
+def softmax_topk(x, k, values=None, indices=None):
+    """Softmax over the last axis of x [..., E], then its k largest entries:
+    (values float32 [..., k] in descending order, indices int32 [..., k])."""
+    if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPE:
+        raise ValueError("x must be a contiguous GPU tensor of float32/float16/bfloat16")
+    E = x.shape[-1]
+    rows = x.numel() // E if E else 0
+    shape = tuple(x.shape[:-1]) + (int(k),)
+    values = torch.empty(shape, dtype=torch.float32, device=x.device) if values is None else values
+    indices = torch.empty(shape, dtype=torch.int32, device=x.device) if indices is None else indices
+    _check(load_library().rf_softmax_topk(_ptr(x), _ptr(values), _ptr(indices), rows, E, int(k),
+                                          _DTYPE[x.dtype], _stream(x)))
+    return values, indices

@@ -11,6 +11,7 @@
 #include "layernorm_kernel.hpp"
 #include "merge_kernel.hpp"
 #include "rope_kernel.hpp"
+#include "topk_kernel.hpp"
 
 namespace {
 
@@ -294,6 +295,38 @@ rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, v
 #undef RF_LN_T
 #undef RF_LN
     return hip_status(hipGetLastError(), "rf_layernorm_fwd launch");
+}
+
+rf_status rf_softmax_topk(const void* x, float* values, int* indices, int rows, int E, int k, int dtype,
+                          hipStream_t stream) {
+    if (rows < 0) return fail(RF_ERR_INVALID_ARG, "rows must be >= 0 (got %d)", rows);
+    if (dtype != RF_F32 && dtype != RF_F16 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (E < 1 || E > 64 * rf::TOPK_MAX_VPL)
+        return fail(RF_ERR_UNSUPPORTED, "E = %d not supported (1 .. %d)", E, 64 * rf::TOPK_MAX_VPL);
+    if (k < 1 || k > E || k > rf::TOPK_MAX_K)
+        return fail(RF_ERR_INVALID_ARG, "k must be in [1, min(E, %d)] (got %d)", rf::TOPK_MAX_K, k);
+    if (rows == 0) return RF_OK;
+    if (!x || !values || !indices) return fail(RF_ERR_INVALID_ARG, "null pointer");
+    if (((uintptr_t)x & (dtype == RF_F32 ? 3u : 1u)) || ((uintptr_t)values & 3u) || ((uintptr_t)indices & 3u))
+        return fail(RF_ERR_INVALID_ARG, "misaligned pointer");
+    const int rpb = rf::TOPK_THREADS / 64;
+    dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+    const int vpl = (E + 63) / 64;
+#define RF_TK(TYPE, N)                                                                                       \
+    hipLaunchKernelGGL((rf::softmax_topk_kernel<TYPE, N>), grid, dim3(rf::TOPK_THREADS), 0, stream, (const TYPE*)x, \
+                       values, indices, rows, E, k)
+#define RF_TK_T(TYPE)                   \
+    if (vpl <= 1) RF_TK(TYPE, 1);       \
+    else if (vpl <= 2) RF_TK(TYPE, 2);  \
+    else if (vpl <= 4) RF_TK(TYPE, 4);  \
+    else if (vpl <= 8) RF_TK(TYPE, 8);  \
+    else RF_TK(TYPE, 16)
+    if (dtype == RF_F32) { RF_TK_T(float); }
+    else if (dtype == RF_F16) { RF_TK_T(_Float16); }
+    else { RF_TK_T(__bf16); }
+#undef RF_TK_T
+#undef RF_TK
+    return hip_status(hipGetLastError(), "rf_softmax_topk launch");
 }
 
 const char* rf_status_string(rf_status s) {

@@ -199,6 +199,24 @@ def run_layernorm(steps, warmup):
             "alg_mb": byts / 1e6}
 
 
+def run_topk(steps, warmup):
+    """rf_softmax_topk on the router workload (logits read once; values and
+    indices written)."""
+    import torch
+    import attention_pass_cascaded_amd as rf
+    from workloads import TOPK_WORKLOAD as w, gen_logits
+    x = gen_logits(w["rows"], w["E"], w["dtype"], w["seed"], device="cuda")
+    vals = torch.empty((w["rows"], w["k"]), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w["rows"], w["k"]), dtype=torch.int32, device="cuda")
+    ms = time_loop(lambda: rf.softmax_topk(x, w["k"], values=vals, indices=idx), steps, warmup)
+    byts = x.numel() * x.element_size() + 8 * w["rows"] * w["k"]
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": w["name"], "ms": ms, "GB/s": gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+            "alg_mb": byts / 1e6}
+
+
 def run_decode(w, steps, warmup):
     import torch
     import attention_pass_cascaded_amd as rf
@@ -344,6 +362,7 @@ def main():
     ap.add_argument("--only", default=None, help="time a single workload (for profiling runs)")
     ap.add_argument("--only-bwd", default=None, metavar="WORKLOAD", help="time the backward of one prefill workload")
     ap.add_argument("--only-layernorm", action="store_true", help="time the LayerNorm workload only")
+    ap.add_argument("--only-topk", action="store_true", help="time the softmax-TopK workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads of batch 0 for the oracle (0: whole workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -369,6 +388,9 @@ def main():
         rotation_sweep(args.steps, args.warmup)
         return
 
+    if args.only_topk:
+        print(json.dumps(run_topk(args.steps, args.warmup)), flush=True)
+        return
     if args.only_layernorm:
         print(json.dumps(run_layernorm(args.steps, args.warmup)), flush=True)
         return
@@ -396,6 +418,8 @@ def main():
     print(f"# backward {w.name}: {bwd['ms']:.4f} ms, {bwd['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     ln = run_layernorm(args.steps, args.warmup)
     print(f"# layernorm {ln['workload']}: {ln['ms']:.4f} ms, {ln['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
+    tk = run_topk(args.steps, args.warmup)
+    print(f"# softmax-topk {tk['workload']}: {tk['ms']:.4f} ms, {tk['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
     copy_gbs = copy_rate()
     print(f"# device copy: {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
@@ -413,6 +437,7 @@ def main():
         "variants": variants,
         "backward": bwd,
         "layernorm": ln,
+        "softmax_topk": tk,
         "hbm_copy_GB/s": copy_gbs,
     }
     print(json.dumps(line), flush=True)

@@ -207,6 +207,24 @@ rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, v
                            float* mean, float* rstd, int rows, int H, float eps,
                            int dtype, hipStream_t stream);
 
+/*
+ * rf_softmax_topk — softmax followed by TopK, a cascade on the max/+ row of
+ * RedFuser Table 1 (TopK combines with max and shifts with +):
+ *   m = max_e x_e,  l = sum_e exp(x_e - m),  and for the k largest
+ *   p_e = exp(x_e - m) / l: values[r, j] = p and indices[r, j] = e,
+ *   j = 0..k-1 in descending order.
+ * Selection compares the exact input values (the k largest p are the k
+ * largest x); equal values go to the lower index, so the result is unique.
+ * One wavefront per row holds the row in registers: x is read once.
+ * x: [rows, E] of dtype (2-byte aligned for 16-bit, 4 for float32); values:
+ * float32 [rows, k]; indices: int32 [rows, k].  1 <= E <= 1024,
+ * 1 <= k <= min(E, 64) (E above 1024 returns RF_ERR_UNSUPPORTED).  NaN
+ * inputs are not supported.  p is float32 (relative error a few times
+ * 2^-24 * (E + |x - m| log2 e)).
+ */
+rf_status rf_softmax_topk(const void* x, float* values, int* indices, int rows, int E, int k,
+                          int dtype, hipStream_t stream);
+
 /* rf_status_string — static text for a status code. */
 const char* rf_status_string(rf_status s);
 

@@ -27,7 +27,7 @@ import math
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal", "alibi_slopes", "gen_grad_out",
-           "LN_WORKLOAD", "gen_layernorm"]
+           "LN_WORKLOAD", "gen_layernorm", "TOPK_WORKLOAD", "gen_logits"]
 
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -140,3 +140,16 @@ def gen_layernorm(rows, H, dtype, seed, device="cpu"):
     gamma = 1.0 + 0.1 * torch.randn((H,), generator=g, dtype=torch.float32, device=device)
     beta = 0.1 * torch.randn((H,), generator=g, dtype=torch.float32, device=device)
     return (z * spread + off).to(dtype), gamma.to(dtype), beta.to(dtype)
+
+
+# Softmax -> TopK (the max/+ cascade): the pages give no shape, so the chosen
+# one is a mixture-of-experts router: 16384 tokens over 256 experts, top 8.
+TOPK_WORKLOAD = dict(name="softmax_topk_bf16_r16384_e256_k8", rows=16384, E=256, k=8, dtype="bf16", seed=7)
+
+
+def gen_logits(rows, E, dtype, seed, device="cpu"):
+    """Router logits: 2 * N(0,1) float32, cast to ``dtype`` (bf16 makes ties common)."""
+    if isinstance(dtype, str):
+        dtype = _DT[dtype]
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    return (2.0 * torch.randn((rows, E), generator=g, dtype=torch.float32, device=device)).to(dtype)
