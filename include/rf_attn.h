@@ -215,7 +215,8 @@ rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, v
  *   j = 0..k-1 in descending order.
  * Selection compares the exact input values (the k largest p are the k
  * largest x); equal values go to the lower index, so the result is unique.
- * One wavefront per row holds the row in registers: x is read once.
+ * A group of 16 lanes (E <= 256, k <= 16) or a whole wavefront per row
+ * holds the row in registers: x is read once.
  * x: [rows, E] of dtype (2-byte aligned for 16-bit, 4 for float32); values:
  * float32 [rows, k]; indices: int32 [rows, k].  1 <= E <= 1024,
  * 1 <= k <= min(E, 64) (E above 1024 returns RF_ERR_UNSUPPORTED).  NaN
