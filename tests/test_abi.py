@@ -125,3 +125,47 @@ def test_oracle_not_reachable_from_product_package():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_rope_rotate_rejects_bad_arguments(lib):
+    assert lib.rf_rope_rotate(FAKE, FAKE, 1, 4, 64, 0.0, 0, 1, None) == B.RF_ERR_INVALID_ARG   # base <= 0
+    assert lib.rf_rope_rotate(FAKE, FAKE, 1, 4, 96, 1e4, 0, 1, None) == B.RF_ERR_UNSUPPORTED   # D
+    assert lib.rf_rope_rotate(None, FAKE, 1, 4, 64, 1e4, 0, 1, None) == B.RF_ERR_INVALID_ARG
+    assert lib.rf_rope_rotate(FAKE, FAKE, 1, 4, 64, 1e4, -1, 1, None) == B.RF_ERR_INVALID_ARG   # offset
+    assert lib.rf_rope_rotate(None, None, 0, 4, 64, 1e4, 0, 1, None) == B.RF_OK                 # empty
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    args = [FAKE] * 10
+    # float32 inputs have no backward instance
+    st = lib.rf_attn_bwd(*args, 1, 2, 2, 8, 8, 64, 0.125, 1, 0, 0.0, None, 0, None)  # dtype 0: float32
+    assert st == B.RF_ERR_UNSUPPORTED and b"float16 and bfloat16" in lib.rf_last_error()
+    # missing dk
+    a = list(args)
+    a[7] = None
+    st = lib.rf_attn_bwd(*a, 1, 2, 2, 8, 8, 64, 0.125, 1, 0, 0.0, None, 1, None)
+    assert st == B.RF_ERR_INVALID_ARG and b"dk and dv" in lib.rf_last_error()
+    # missing workspace
+    a = list(args)
+    a[9] = None
+    st = lib.rf_attn_bwd(*a, 1, 2, 2, 8, 8, 64, 0.125, 1, 0, 0.0, None, 1, None)
+    assert st == B.RF_ERR_INVALID_ARG and b"workspace" in lib.rf_last_error()
+    assert lib.rf_attn_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+    assert lib.rf_attn_bwd_workspace_bytes(-1, 3, 5) == 0
+
+
+def test_layernorm_rejects_bad_arguments(lib):
+    assert lib.rf_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 1e-5, 2, None) == B.RF_ERR_UNSUPPORTED
+    assert b"multiple of 8" in lib.rf_last_error()
+    assert lib.rf_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32768, 1e-5, 2, None) == B.RF_ERR_UNSUPPORTED
+    assert lib.rf_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, -1.0, 2, None) == B.RF_ERR_INVALID_ARG
+    assert lib.rf_layernorm_fwd(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 64, 1e-5, 2, None) == B.RF_ERR_INVALID_ARG
+    assert lib.rf_layernorm_fwd(None, None, None, None, None, None, 0, 64, 1e-5, 2, None) == B.RF_OK
+
+
+def test_softmax_topk_rejects_bad_arguments(lib):
+    assert lib.rf_softmax_topk(FAKE, FAKE, FAKE, 4, 16, 17, 2, None) == B.RF_ERR_INVALID_ARG    # k > E
+    assert lib.rf_softmax_topk(FAKE, FAKE, FAKE, 4, 256, 65, 2, None) == B.RF_ERR_INVALID_ARG   # k > 64
+    assert lib.rf_softmax_topk(FAKE, FAKE, FAKE, 4, 2048, 8, 2, None) == B.RF_ERR_UNSUPPORTED   # E
+    assert lib.rf_softmax_topk(FAKE, None, FAKE, 4, 256, 8, 2, None) == B.RF_ERR_INVALID_ARG
+    assert lib.rf_softmax_topk(None, None, None, 0, 256, 8, 2, None) == B.RF_OK
