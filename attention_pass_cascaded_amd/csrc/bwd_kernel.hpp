@@ -44,6 +44,18 @@ struct BwdParams {
 
 constexpr int BWD_THREADS = 256;
 
+// Waves per SIMD the D = 64 dq and dk/dv kernels are compiled for, and the
+// query tile of the dk/dv kernel at D = 64 (tuning knobs, measured).
+#ifndef RF_BWD_DQ_WAVES
+#define RF_BWD_DQ_WAVES 2
+#endif
+#ifndef RF_BWD_KV_WAVES
+#define RF_BWD_KV_WAVES 2
+#endif
+#ifndef RF_BWD_BQ64
+#define RF_BWD_BQ64 64
+#endif
+
 // ---------------------------------------------------------------- D_i
 template <typename T, int D>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_rowterm_kernel(const T* o, const T* dout, float* drow, long long rows) {
@@ -84,7 +96,7 @@ __device__ __forceinline__ void rope_unrotate(double inv_period, int pos, float&
 // P^T, dP^T and dS^T sit in the lane's registers and feed dQ^T += K^T . dS^T
 // as the B operand, with K^T read from the K tile by the LDS transpose read.
 template <typename T, int D, bool ROPE, bool ALIBI>
-__global__ __launch_bounds__(FWD_THREADS, D == 64 ? 2 : 1) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(FWD_THREADS, D == 64 ? RF_BWD_DQ_WAVES : 1) void attn_bwd_dq_kernel(BwdParams p) {
     using C = FwdCfg<T, D, false>;
     constexpr int BN = C::BN;
     constexpr int EPC = C::EPC;
@@ -372,7 +384,7 @@ constexpr int BWD_BK = 128;  // keys per work-group
 
 template <typename T, int D>
 struct BwdKvCfg {
-    static constexpr int BQ = D == 64 ? 64 : 32;      // queries per tile
+    static constexpr int BQ = D == 64 ? RF_BWD_BQ64 : 32;  // queries per tile
     static constexpr int NQB = BQ / 32;
     static constexpr int EPC = 8;
     static constexpr int CPR = D / EPC;
@@ -384,7 +396,7 @@ struct BwdKvCfg {
 };
 
 template <typename T, int D, bool ROPE, bool ALIBI>
-__global__ __launch_bounds__(BWD_THREADS, D == 64 ? 2 : 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(BWD_THREADS, D == 64 ? RF_BWD_KV_WAVES : 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     using C = BwdKvCfg<T, D>;
     constexpr int BQ = C::BQ;
     constexpr int NQB = C::NQB;
