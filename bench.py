@@ -354,15 +354,6 @@ def copy_rate(nbytes: int = 1 << 30, steps: int = 20) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def read_rate(nbytes: int = 1 << 31, steps: int = 20) -> float:
-    """GB/s of a plain device reduction (torch sum) over a large buffer: the
-    read-only HBM rate a streaming kernel can practically reach."""
-    import torch
-    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
-    ms = time_loop(lambda: src.sum(dtype=torch.float32), steps, 3)
-    return nbytes / (ms * 1e-3) / 1e9
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -430,8 +421,7 @@ def main():
     tk = run_topk(args.steps, args.warmup)
     print(f"# softmax-topk {tk['workload']}: {tk['ms']:.4f} ms, {tk['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
     copy_gbs = copy_rate()
-    read_gbs = read_rate()
-    print(f"# device copy: {copy_gbs:.0f} GB/s, device sum (read only): {read_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"# device copy: {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
 
     line = {
@@ -449,7 +439,6 @@ def main():
         "layernorm": ln,
         "softmax_topk": tk,
         "hbm_copy_GB/s": copy_gbs,
-        "hbm_read_GB/s": read_gbs,
     }
     print(json.dumps(line), flush=True)
 
