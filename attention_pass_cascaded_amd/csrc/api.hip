@@ -310,26 +310,29 @@ rf_status rf_softmax_topk(const void* x, float* values, int* indices, int rows, 
     if (((uintptr_t)x & (dtype == RF_F32 ? 3u : 1u)) || ((uintptr_t)values & 3u) || ((uintptr_t)indices & 3u))
         return fail(RF_ERR_INVALID_ARG, "misaligned pointer");
     // 16 lanes per row when the row fits 16 values per lane and k <= 16
+    // (measured: 8 lanes with 32 values each runs fewer instructions per row
+    // but half the wavefronts, and was slower)
     const bool narrow = E <= 16 * rf::TOPK_MAX_VPL && k <= 16;
     const int lpr = narrow ? 16 : 64;
     const int rpb = (rf::TOPK_THREADS / 64) * (64 / lpr);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     const int vpl = (E + lpr - 1) / lpr;
-#define RF_TK(TYPE, N, L)                                                                                       \
-    hipLaunchKernelGGL((rf::softmax_topk_kernel<TYPE, N, L>), grid, dim3(rf::TOPK_THREADS), 0, stream,           \
-                       (const TYPE*)x, values, indices, rows, E, k)
-#define RF_TK_V(TYPE, L)                   \
-    if (vpl <= 1) RF_TK(TYPE, 1, L);       \
-    else if (vpl <= 2) RF_TK(TYPE, 2, L);  \
-    else if (vpl <= 4) RF_TK(TYPE, 4, L);  \
-    else if (vpl <= 8) RF_TK(TYPE, 8, L);  \
-    else RF_TK(TYPE, 16, L)
-#define RF_TK_T(TYPE)                      \
-    if (narrow) { RF_TK_V(TYPE, 16); }     \
-    else { RF_TK_V(TYPE, 64); }
-    if (dtype == RF_F32) { RF_TK_T(float); }
-    else if (dtype == RF_F16) { RF_TK_T(_Float16); }
-    else { RF_TK_T(__bf16); }
+#define RF_TK(KERNEL, TYPE, N, L)                                                                          \
+    hipLaunchKernelGGL((rf::KERNEL<TYPE, N, L>), grid, dim3(rf::TOPK_THREADS), 0, stream, (const TYPE*)x, values, \
+                       indices, rows, E, k)
+#define RF_TK_V(KERNEL, TYPE, L)                   \
+    if (vpl <= 1) RF_TK(KERNEL, TYPE, 1, L);       \
+    else if (vpl <= 2) RF_TK(KERNEL, TYPE, 2, L);  \
+    else if (vpl <= 4) RF_TK(KERNEL, TYPE, 4, L);  \
+    else if (vpl <= 8) RF_TK(KERNEL, TYPE, 8, L);  \
+    else RF_TK(KERNEL, TYPE, 16, L)
+#define RF_TK_T(KERNEL, TYPE)                  \
+    if (narrow) { RF_TK_V(KERNEL, TYPE, 16); } \
+    else { RF_TK_V(KERNEL, TYPE, 64); }
+    // 16-bit inputs: packed (value, index) keys; float32: (value, index) pairs
+    if (dtype == RF_F32) { RF_TK_T(softmax_topk_kernel, float); }
+    else if (dtype == RF_F16) { RF_TK_T(softmax_topk16_kernel, _Float16); }
+    else { RF_TK_T(softmax_topk16_kernel, __bf16); }
 #undef RF_TK_T
 #undef RF_TK_V
 #undef RF_TK

@@ -100,4 +100,118 @@ __global__ __launch_bounds__(TOPK_THREADS) void softmax_topk_kernel(const T* __r
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit inputs: every element becomes one 32-bit key
+//   key = (order-preserving bits of x) << 16 | (0xFFFF - e),
+// so "larger value, then lower index" is plain unsigned order and each
+// comparison of the selection is a single v_max_u32.  The row-group
+// reductions use DPP lane moves inside a 16-lane row (quad xor 1, quad xor 2,
+// half-row mirror, row mirror: after the four steps every lane of the row
+// holds the row's result) instead of LDS permutes; a 64-lane group adds two
+// exchanges across rows.  The first winner is the row max m, so level 1 needs
+// no pass of its own.
+
+// x's bits mapped so that unsigned order is the order of the values; -0 and
+// +0 share a key.  Finite inputs only (NaN has no place in the order).
+__device__ __forceinline__ unsigned topk_mono16(unsigned b) {
+    b = (b == 0x8000u) ? 0u : b;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+__device__ __forceinline__ unsigned topk_unmono16(unsigned m) {
+    return (m & 0x8000u) ? (m & 0x7FFFu) : (~m & 0xFFFFu);
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned topk_dpp(unsigned x) {
+    return (unsigned)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// max over the row group of LPR lanes (16 or 64), in every lane of the group
+template <int LPR>
+__device__ __forceinline__ unsigned topk_group_max(unsigned v) {
+    v = max(v, topk_dpp<DPP_QUAD_XOR1>(v));
+    v = max(v, topk_dpp<DPP_QUAD_XOR2>(v));
+    v = max(v, topk_dpp<DPP_ROW_HALF_MIRROR>(v));
+    v = max(v, topk_dpp<DPP_ROW_MIRROR>(v));
+    if constexpr (LPR == 64) {
+        v = max(v, (unsigned)__shfl_xor((int)v, 16, 64));
+        v = max(v, (unsigned)__shfl_xor((int)v, 32, 64));
+    }
+    return v;
+}
+// sum over the row group; every lane gets the same bits (each step adds the
+// same two partial sums in every lane)
+template <int LPR>
+__device__ __forceinline__ float topk_group_sum(float v) {
+    v += __uint_as_float(topk_dpp<DPP_QUAD_XOR1>(__float_as_uint(v)));
+    v += __uint_as_float(topk_dpp<DPP_QUAD_XOR2>(__float_as_uint(v)));
+    v += __uint_as_float(topk_dpp<DPP_ROW_HALF_MIRROR>(__float_as_uint(v)));
+    v += __uint_as_float(topk_dpp<DPP_ROW_MIRROR>(__float_as_uint(v)));
+    if constexpr (LPR == 64) {
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+    }
+    return v;
+}
+
+template <typename T, int VPL, int LPR>
+__global__ __launch_bounds__(TOPK_THREADS) void softmax_topk16_kernel(const T* __restrict__ x, float* __restrict__ values,
+                                                                      int* __restrict__ indices, int rows, int E,
+                                                                      int k) {
+    static_assert(sizeof(T) == 2, "16-bit inputs");
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int RPW = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR;
+    const long long row = ((long long)blockIdx.x * (TOPK_THREADS / 64) + (threadIdx.x >> 6)) * RPW + lane / LPR;
+    const bool row_ok = row < rows;
+    const unsigned short* xr = (const unsigned short*)x + (row_ok ? row : 0) * (long long)E;
+
+    // lane `sub` of the group owns elements sub, sub + LPR, ...; absent ones
+    // get key 0 (below every present key) and x = -inf
+    unsigned key[VPL];
+    float xv[VPL];
+    unsigned best = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = sub + LPR * i;
+        const unsigned b = xr[min(e, E - 1)];  // in-row address for every lane: no branch
+        xv[i] = e < E ? to_f32(__builtin_bit_cast(T, (unsigned short)b)) : -INFINITY;
+        key[i] = e < E ? (topk_mono16(b) << 16) | (0xFFFFu - (unsigned)e) : 0u;
+        best = max(best, key[i]);
+    }
+    // level 1: the first winner is the row max
+    unsigned win = topk_group_max<LPR>(best);
+    const float m = to_f32(__builtin_bit_cast(T, (unsigned short)topk_unmono16(win >> 16)));
+    const float msub = m == -INFINITY ? 0.f : m;
+    // level 2: sum of exponentials relative to m
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) l += fast_exp2((xv[i] - msub) * LOG2E);
+    l = topk_group_sum<LPR>(l);
+    const float inv_l = 1.f / l;
+
+    // level 3: k - 1 more rounds; the taken key drops to 0
+    unsigned mine = sub == 0 ? win : 0u;
+    for (int j = 1; j < k; ++j) {
+        best = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            key[i] = key[i] == win ? 0u : key[i];
+            best = max(best, key[i]);
+        }
+        win = topk_group_max<LPR>(best);
+        mine = sub == j ? win : mine;
+    }
+    if (row_ok && sub < k) {
+        const float v = to_f32(__builtin_bit_cast(T, (unsigned short)topk_unmono16(mine >> 16)));
+        values[row * k + sub] = fast_exp2((v - msub) * LOG2E) * inv_l;
+        indices[row * k + sub] = (int)(0xFFFFu - (mine & 0xFFFFu));
+    }
+}
+
 }  // namespace rf

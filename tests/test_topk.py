@@ -33,10 +33,14 @@ def check(x, k, vals, idx):
 
 
 CASES = [
-    # dtype, rows, E, k
+    # dtype, rows, E, k   (16-lane groups for E <= 256 and k <= 16, else whole
+    # wavefronts; 16-bit rows take the packed-key kernel, f32 the pair kernel)
     ("bf16", 33, 256, 8),
     ("bf16", 7, 1024, 64),
     ("f16", 50, 100, 5),
+    ("f16", 9, 7, 3),
+    ("bf16", 17, 200, 12),
+    ("f16", 40, 256, 16),
     ("f32", 9, 64, 64),
     ("f32", 5, 1, 1),
     ("bf16", 3, 777, 13),
@@ -58,6 +62,21 @@ def test_softmax_topk_all_ties():
     torch.cuda.synchronize()
     assert torch.equal(idx.cpu(), torch.arange(10, dtype=torch.int32).repeat(4, 1))
     assert torch.allclose(vals.cpu(), torch.full((4, 10), 1.0 / 96), rtol=1e-6)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("k", [4, 12])
+def test_softmax_topk_signed_zeros_and_neg_inf(dt, k):
+    # -0 and +0 are equal values (ties go to the lower index); -inf entries
+    # are valid and get p = 0
+    row = [-0.0, 0.0, -0.0, 1.0, float("-inf"), -0.5, 0.0, -0.0, float("-inf"), -3.0] * 5
+    x = torch.tensor([row, row[::-1]], dtype=getattr(torch, {"bf16": "bfloat16", "f16": "float16"}[dt]))
+    vals, idx = rf.softmax_topk(x.cuda(), k)
+    torch.cuda.synchronize()
+    check(x, k, vals, idx)
+    # the five 1.0 entries first, then the zeros of either sign by index
+    expect = [3, 13, 23, 33, 43, 0, 1, 2, 6, 7, 10, 11][:k]
+    assert idx[0].tolist() == expect
 
 
 def test_softmax_topk_rejects_bad_k():
