@@ -78,6 +78,9 @@ def fwd(lib, **kw):
     (dict(q=ctypes.c_void_p(4098)), B.RF_ERR_INVALID_ARG, "aligned"),
     (dict(o=None), B.RF_ERR_INVALID_ARG, "required"),
     (dict(lse=None), B.RF_ERR_INVALID_ARG, "required"),
+    # one KV head of 2^31 bytes (bf16, D = 128) is one key row too many
+    (dict(D=128, Nk=(1 << 31) // 256, dtype=2), B.RF_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(D=64, Nk=(1 << 31) // 256, dtype=0), B.RF_ERR_UNSUPPORTED, "2 GiB"),
 ])
 def test_fwd_rejects_bad_arguments(lib, kw, status, needle):
     assert fwd(lib, **kw) == status
