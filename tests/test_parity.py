@@ -65,6 +65,12 @@ FWD_CASES = [
     ("bf16", 128, 1, 4, 1, 200, 200, "causal", 0, 10000.0),
     ("bf16", 64, 1, 2, 2, 190, 190, "none", 0, 500.0),
     ("bf16", 128, 1, 2, 2, 64, 64, "none", 0, 0.0),
+    # RoPE over many tiles and at large positions (up to 70,000 keys, so
+    # angles of thousands of revolutions), with windows starting mid-tile
+    ("f16", 64, 1, 2, 2, 64, 2100, "causal", 0, 10000.0),
+    ("bf16", 64, 1, 2, 1, 40, 1500, "none", 0, 10000.0),
+    ("f16", 64, 1, 2, 2, 100, 1400, "sliding", 1200, 10000.0),
+    ("f16", 64, 1, 1, 1, 16, 70000, "causal", 0, 10000.0),
     ("f32", 64, 1, 1, 1, 256, 256, "none", 0, 0.0),
     ("f32", 64, 1, 2, 2, 100, 100, "causal", 0, 10000.0),
     ("f32", 128, 1, 2, 1, 77, 150, "sliding", 40, 0.0),
