@@ -43,7 +43,9 @@
  *    nothing.  RF_ERR_INVALID_ARG: null pointer for a non-empty tensor,
  *    negative size, Hq % Hkv != 0, scale negative or not finite, window < 1
  *    with the sliding mask, unknown mask or dtype, misaligned pointer.
- *    RF_ERR_UNSUPPORTED: D not in {64, 128}.  RF_ERR_HIP: a launch failed.
+ *    RF_ERR_UNSUPPORTED: D not in {64, 128}, or one KV head of 2 GiB or more
+ *    (Nk * D * element size >= 2^31: in-head offsets are 32-bit).
+ *    RF_ERR_HIP: a launch failed.
  *    rf_last_error() returns a thread-local message for the last non-OK
  *    status of the calling thread.
  *  - All entry points are thread-safe and keep no state between calls.
