@@ -2,8 +2,8 @@
 // and level-2 sum of the cascade applied over chunks, RedFuser Fig. 4):
 //   M = max_c lse_c,  lse = M + ln sum_c exp(lse_c - M),
 //   O = sum_c exp(lse_c - lse) O_c,  rounded once to the output dtype.
-// One work-group per row.  Every thread first folds the row's chunk lse values
-// (broadcast reads) into the running max and rescaled sum; then the threads
+// One work-group per row.  Each wavefront first reduces the row's chunk lse
+// values (max, then the sum of 2^(lse_c - max)) across its lanes; then the threads
 // split the chunks into NSL slices, each thread streaming 4 consecutive d of
 // its chunks with 16-byte loads (all in flight at once), and the slices are
 // summed through LDS.
@@ -14,6 +14,31 @@
 namespace rf {
 
 constexpr int MRG_THREADS = 256;
+
+// Wavefront-wide max and sum with DPP moves inside 16-lane rows (quad xor 1,
+// quad xor 2, half-row mirror, row mirror), then the exchanges 16 and 32 lanes
+// away; each step combines the same two values in both lanes of a pair, so
+// every lane ends with identical bits.
+template <int CTRL>
+__device__ __forceinline__ float merge_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float merge_wave_max(float v) {
+    v = fmaxf(v, merge_dpp<0xB1>(v));
+    v = fmaxf(v, merge_dpp<0x4E>(v));
+    v = fmaxf(v, merge_dpp<0x141>(v));
+    v = fmaxf(v, merge_dpp<0x140>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, swap_halves(v));
+}
+__device__ __forceinline__ float merge_wave_sum(float v) {
+    v += merge_dpp<0xB1>(v);
+    v += merge_dpp<0x4E>(v);
+    v += merge_dpp<0x141>(v);
+    v += merge_dpp<0x140>(v);
+    v += __shfl_xor(v, 16, 64);
+    return v + swap_halves(v);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(MRG_THREADS) void lse_merge_kernel(const float* __restrict__ o_part,
@@ -32,16 +57,18 @@ __global__ __launch_bounds__(MRG_THREADS) void lse_merge_kernel(const float* __r
     const int d4 = tid % TPS;
     const float* lp = lse_part + row * S;
 
-    // level 1 and level 2 over the chunks, folded incrementally (log2 units)
-    float m = -INFINITY, tot = 0.f;
-    for (int c = 0; c < S; ++c) {
-        const float x = lp[c] * LOG2E;
-        const float mn = fmaxf(m, x);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        tot = tot * fast_exp2(m - mu) + fast_exp2(x - mu);
-        m = mn;
-    }
+    // level 1 and level 2 over the chunks (log2 units): every wavefront takes
+    // the row's chunk lse values one per lane (chunks c, c + 64, ...) and
+    // reduces them with lane butterflies, so all lanes hold the same bits
+    const int lane = tid & 63;
+    float m = -INFINITY;
+    for (int c = lane; c < S; c += 64) m = fmaxf(m, lp[c] * LOG2E);
+    m = merge_wave_max(m);
     const bool live = m != -INFINITY;
+    float tot = 0.f;
+    if (live)
+        for (int c = lane; c < S; c += 64) tot += fast_exp2(fmaf(lp[c], LOG2E, -m));
+    tot = merge_wave_sum(tot);
     const float lse2 = live ? m + fast_log2(tot) : 0.f;
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
