@@ -59,7 +59,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15;   // MFMA column: query row of this lane
     const int q = lane >> 4;   // lane group: contraction slots 8q..8q+7
 
@@ -80,8 +80,6 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
     // K and V of this (batch, KV head); rows past Nk read as zeros.  Rows in
     // [khi, Nk) belong to the next chunk: they are loaded but masked out.
     const int kv_bytes = p.Nk * D * (int)sizeof(T);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)p.k + kv_base, kv_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)p.v + kv_base, kv_bytes);
 
     // ---- this lane's query row: head g*G + n/Nq, query n%Nq
     const bool row_ok = n < rows;
@@ -91,17 +89,54 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
     const int lim_lo = p.mask == RF_MASK_SLIDING ? my_pos - p.window + 1 : -(1 << 30);
     const float slope2 = ALIBI ? p.alibi[g * G + gi] * LOG2E : 0.f;  // log2 units
 
+    // Q is loaded first and converted after the first K/V loads are issued
+    VecT qraw[NKS];
+    {
+        const T* qrow = (const T*)p.q + (((size_t)b * p.Hq + g * G + gi) * p.Nq + qi) * D;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qraw[ks] = *(const VecT*)(qrow + 32 * ks + 8 * q);
+    }
+
+    // K into A-operand registers, V into registers bound for LDS.  Each set is
+    // reloaded for the wave's next sub-block as soon as this one has consumed
+    // it, so the loads stay in flight under the softmax and P.V of this step.
+    // The loads are issued unconditionally (no branch for the compiler's wait
+    // counting to merge); past the wave's last sub-block they go through a
+    // zero-size descriptor, which returns zeros without touching memory.
+    VecT ka[2][NKS];
+    uint4 vr[VLD];
+    auto load_k = [&](int k0, bool live) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const T*)p.k + kv_base, live ? kv_bytes : 0);
+#pragma unroll
+        for (int kgp = 0; kgp < 2; ++kgp) {
+            const int key = k0 + 16 * kgp + n;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                ka[kgp][ks] = __builtin_bit_cast(VecT, buf_load16(rs, (key * D + 32 * ks + 8 * q) * (int)sizeof(T)));
+        }
+    };
+    auto load_v = [&](int k0, bool live) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const T*)p.v + kv_base, live ? kv_bytes : 0);
+#pragma unroll
+        for (int it = 0; it < VLD; ++it) {
+            const int u = it * 64 + lane;
+            vr[it] = buf_load16(rs, ((k0 + u / CPR) * D + (u % CPR) * 8) * (int)sizeof(T));
+        }
+    };
+    constexpr int STRIDE = DM_SUB * DM_WAVES;
+    const int k_first = klo + DM_SUB * wave;
+    load_k(k_first, k_first < khi);
+    load_v(k_first, k_first < khi);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the wait on Q
+
     // Q^T operand: lane holds q[row][32*ks + 8*q + i]; RoPE partner is ks +- NKS/2.
     VecT qv[NKS], qlo[SPLITK ? NKS : 1];
     {
-        const T* qrow = (const T*)p.q + (((size_t)b * p.Hq + g * G + gi) * p.Nq + qi) * D;
         float qf[NKS][8];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const VecT x = *(const VecT*)(qrow + 32 * ks + 8 * q);
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qf[ks][i] = row_ok ? to_f32(x[i]) : 0.f;
-        }
+            for (int i = 0; i < 8; ++i) qf[ks][i] = row_ok ? to_f32(qraw[ks][i]) : 0.f;
         if (ROPE) {
 #pragma unroll
             for (int ks = 0; ks < NKS / 2; ++ks)
@@ -141,22 +176,9 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
     const int tr_row = 4 * q + (n >> 2);
     const int tr_col = 4 * (n & 3);
 
-    for (int k0 = klo + DM_SUB * wave; k0 < khi; k0 += DM_SUB * DM_WAVES) {
-        // ---- issue the loads: K into A-operand registers, V into registers for LDS
-        VecT ka[2][NKS];
-#pragma unroll
-        for (int kgp = 0; kgp < 2; ++kgp) {
-            const int key = k0 + 16 * kgp + n;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                ka[kgp][ks] = __builtin_bit_cast(VecT, buf_load16(krs, (key * D + 32 * ks + 8 * q) * (int)sizeof(T)));
-        }
-        uint4 vr[VLD];
-#pragma unroll
-        for (int it = 0; it < VLD; ++it) {
-            const int u = it * 64 + lane;
-            vr[it] = buf_load16(vrs, ((k0 + u / CPR) * D + (u % CPR) * 8) * (int)sizeof(T));
-        }
+
+    for (int k0 = k_first; k0 < khi; k0 += STRIDE) {
+        const bool more = k0 + STRIDE < khi;
 
         // ---- RoPE on K (pairs are in-lane: ks and ks + NKS/2)
         VecT kalo[SPLITK ? 2 : 1][SPLITK ? NKS : 1];
@@ -197,12 +219,15 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
             }
         }
 
+        load_k(k0 + STRIDE, more);
+
         // ---- V tile into this wave's LDS buffer (row-major, padded rows)
 #pragma unroll
         for (int it = 0; it < VLD; ++it) {
             const int u = it * 64 + lane;
             *(uint4*)(vb + (u / CPR) * VS + (u % CPR) * 8) = vr[it];
         }
+        load_v(k0 + STRIDE, more);
 
         // ---- mask (ragged chunk end and causal / window bounds), tile max
         const int rel_hi = lim_hi - k0 - 4 * q;
