@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "bwd_kernel.hpp"
@@ -33,6 +34,21 @@ rf_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Compute units of the current device, cached per device (0 if the query fails).
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev >= 64) {
+        int n = 0;
+        return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cache[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
+}
 
 // theta_i / (2 pi) = base^(-2i/D) / (2 pi), i < D/2, in double on the host.
 rf::RopeTable rope_table(float base, int D) {
@@ -83,6 +99,7 @@ rf_status check_attn(const void* q, const void* k, const void* v, int B, int Hq,
     if (p.rope_base > 0.f) p.rope = rope_table(p.rope_base, D);
     p.num_splits = 1;
     p.split_len = Nk;
+    p.cu_count = device_cu_count();
     return RF_OK;
 }
 

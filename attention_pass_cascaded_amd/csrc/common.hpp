@@ -49,6 +49,8 @@ struct AttnParams {
     int num_splits;    // 1 when not splitting
     int split_len;     // keys per chunk, ceil(Nk / num_splits)
     int split_mode;    // 1: write normalised partials + chunk lse
+    int cu_count;      // compute units of the device (work-group placement), 0 if unknown
+    int launch_runs;   // work-groups per CU resident at launch (set by the forward launcher)
 };
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -82,7 +82,14 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
 
     // Work-group order (one-dimensional grid of B*Hq*S*nqb).
     //  causal: every head's heaviest (latest) query blocks first, then lighter
-    //    ones, so the uneven blocks balance across the CUs;
+    //    ones, so the uneven blocks balance across the CUs.  The groups that
+    //    start at launch are placed statically: group pid goes to the CU
+    //    numbered pid mod P (P CUs), so a CU receives items pid, pid + P,
+    //    pid + 2P, ...  When the whole grid is resident at launch, every other
+    //    run of P items is taken in reverse (snake order), which gives each CU
+    //    a heavy item from one run and a light one from the next instead of
+    //    items of the same rank.  A larger grid keeps the plain order: its
+    //    later groups start wherever a slot frees, which balances by itself;
     //  no mask / sliding window (every block costs the same): the dispatcher
     //    deals work-groups round-robin over the XCDs (each with its own L2), so
     //    renumber to give every XCD a contiguous run of one head's query blocks
@@ -93,8 +100,14 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     int qb, bx;  // bx = (b * Hq + h) * S + split
     if (p.mask == RF_MASK_CAUSAL) {
         const int heads = G / nqb;
-        qb = nqb - 1 - pid / heads;
-        bx = pid % heads;
+        const int P = p.cu_count;
+        int item = pid;  // index in heaviest-first order
+        if (P > 0 && (long long)P * p.launch_runs >= G) {
+            const int run = pid / P;
+            if ((run & 1) && run < G / P) item = run * P + (P - 1 - pid % P);
+        }
+        qb = nqb - 1 - item / heads;
+        bx = item % heads;
     } else {
         const int xcd = pid % NUM_XCD, local = pid / NUM_XCD;
         const int per = G / NUM_XCD, rem = G % NUM_XCD;

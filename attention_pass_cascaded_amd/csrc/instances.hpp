@@ -1,6 +1,8 @@
 // Template instantiation and dispatch on (D, RoPE, rows) for one dtype.
 #pragma once
 
+#include <atomic>
+
 #include "bwd_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "decode_mfma_kernel.hpp"
@@ -11,8 +13,21 @@ namespace rf {
 
 template <typename T, int D, bool ROPE, bool ALIBI>
 hipError_t fwd_launch_one(const AttnParams& p, hipStream_t s) {
+    // work-groups of this instance that fit on one CU (cached; same for every gfx950 device)
+    static std::atomic<int> resident{0};
+    int r = resident.load(std::memory_order_relaxed);
+    if (r == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, attn_fwd_kernel<T, D, ROPE, ALIBI>, FWD_THREADS, 0) != hipSuccess) {
+            r = 0;
+            (void)hipGetLastError();  // a failed query only turns the snake order off
+        }
+        if (r > 0) resident.store(r, std::memory_order_relaxed);
+        else r = 0;
+    }
+    AttnParams q = p;
+    q.launch_runs = r;
     dim3 grid((unsigned)(p.B * p.Hq * p.num_splits * ((p.Nq + FWD_BM - 1) / FWD_BM)));
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI>), grid, dim3(FWD_THREADS), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI>), grid, dim3(FWD_THREADS), 0, s, q);
     return hipGetLastError();
 }
 
