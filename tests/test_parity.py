@@ -88,6 +88,21 @@ def test_fwd_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
     compare(o, lse, ro, rl, TOL[dt], "fwd")
 
 
+@pytest.mark.parametrize("scale", [0.125, 0.69, 0.7, 1.0, 4.0])
+def test_fwd_f16_d64_scale_range_matches_oracle(scale):
+    """fp16, D = 64, no RoPE or ALiBi, over a range of scales with Q tripled
+    so the weights are far from uniform: larger scores must not cost
+    accuracy (the scores are formed from the unscaled fp16 q and k, and the
+    scale is applied in fp32)."""
+    q, k, v = gen_qkv(1, 3, 3, 300, 300, 64, "f16", 5)
+    q = (q.float() * 3).half()
+    print(f"case fwd f16 D=64 scale={scale}", flush=True)
+    for mask in ("causal", "none"):
+        o, lse = run_fwd(q, k, v, scale, mask, 0, 0.0)
+        ro, rl = oracle.attention(q, k, v, scale, mask)
+        compare(o, lse, ro, rl, TOL["f16"], f"scale {scale} {mask}")
+
+
 def test_fwd_empty_keys_gives_zero_and_neg_inf():
     q, k, v = gen_qkv(1, 2, 2, 40, 0, 64, "f16", 1)
     o, lse = run_fwd(q, k, v, 0.125, "none", 0, 0.0)
