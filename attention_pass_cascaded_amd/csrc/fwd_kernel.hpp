@@ -55,9 +55,16 @@ struct FwdCfg {
 #ifndef RF_FWD_WAVES_D64
 #define RF_FWD_WAVES_D64 4
 #endif
+// Waves per SIMD of the plain 16-bit D = 128 instance: its single V buffer
+// (see below) lets 3 work-groups share a CU's LDS.
+#ifndef RF_FWD_WAVES_D128
+#define RF_FWD_WAVES_D128 3
+#endif
 
 template <typename T, int D, bool ROPE, bool ALIBI>
-__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64
+                                          : (D == 128 && sizeof(T) == 2 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D128
+                                                                                           : 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
     using C = FwdCfg<T, D, SPLITK>;
     constexpr bool F32 = C::F32;
@@ -71,12 +78,18 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     constexpr float LN2 = 0.6931471805599453f;
     constexpr float RESCALE_SLACK = 8.0f;  // log2 units
     typedef typename Vec16<T>::type VecT;
+    // V1 (16-bit, D = 128, no RoPE or ALiBi): two K buffers and one V buffer
+    // (52 KB, so 3 work-groups fit a CU), both filled by buffer loads that
+    // write LDS directly.  Tile t's V and tile t+1's K are issued together
+    // once every wave has finished tile t-1's P.V; V(t) lands under tile t's
+    // score products and softmax, and a second barrier precedes the P.V.
+    constexpr bool V1 = D == 128 && !F32 && !ROPE && !ALIBI;
 
-    __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) T smem[V1 ? 2 * C::K_ELEMS + BN * KS : 2 * C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -211,8 +224,36 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         for (int e = 0; e < EPC; ++e) ipd[e] = p.rope.inv_period[cc * EPC + e];
     }
 
-    // ---------------- tile staging (global -> registers -> LDS)
-    uint4 kreg[C::CH], vreg[C::CH];
+    // ---------------- tile staging
+    // V1: one wave load writes 16 bytes per lane, lane-major, i.e. 64
+    // consecutive 16-byte slots of the padded row layout; a lane whose slot is
+    // a row's pad reads past the buffer end and gets zeros.  Otherwise:
+    // global -> registers -> LDS (RoPE rotates K on the way).
+    constexpr int SPR = CPR + 1;                  // 16-byte slots per LDS row (pitch KS)
+    constexpr int NLW = (SPR + FWD_WAVES - 1) / FWD_WAVES;
+    static_assert(!V1 || (BN == 64 && C::K_ELEMS == BN * KS), "one wave load per 64 slots");
+    unsigned dma_off[V1 ? NLW : 1];
+    if constexpr (V1) {
+#pragma unroll
+        for (int i = 0; i < NLW; ++i) {
+            const int p_ = 64 * ((wave + FWD_WAVES * i) % SPR) + lane;
+            const int row = p_ / SPR, ch = p_ % SPR;
+            dma_off[i] = ch < CPR ? (unsigned)((row * D + ch * EPC) * (int)sizeof(T)) : 0x80000000u;
+        }
+    }
+    // the BN rows of K or V from key k0 into dst (a K buffer or the V buffer)
+    auto issue_rows = [&](__amdgpu_buffer_rsrc_t rs, T* dst, int k0) {
+        const unsigned base = (unsigned)k0 * (unsigned)(D * sizeof(T));
+#pragma unroll
+        for (int i = 0; i < NLW; ++i) {
+            const int jj = wave + FWD_WAVES * i;  // wave-uniform
+            if (jj < SPR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + jj * 64 * EPC),
+                                                         16, (int)(base + dma_off[i]), 0, 0, 0);
+        }
+    };
+
+    uint4 kreg[V1 ? 1 : C::CH], vreg[V1 ? 1 : C::CH];
 
     auto load_tile = [&](int k0) {
 #pragma unroll
@@ -300,15 +341,25 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     float l_run = 0.f;
 
     if (ntiles > 0) {
-        load_tile(klo);
-        store_tile(0, klo);
+        if constexpr (V1) {
+            issue_rows(krs, smem, klo);
+        } else {
+            load_tile(klo);
+            store_tile(0, klo);
+        }
     }
 
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = klo + t * BN;
         const int stage = t & 1;
+        if constexpr (V1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(t) landed
         __syncthreads();
-        if (t + 1 < ntiles) load_tile(k0 + BN);
+        if constexpr (V1) {
+            issue_rows(vrs, smem + 2 * C::K_ELEMS, k0);
+            if (t + 1 < ntiles) issue_rows(krs, smem + (stage ^ 1) * C::K_ELEMS, k0 + BN);
+        } else if (t + 1 < ntiles) {
+            load_tile(k0 + BN);
+        }
 
         // wave-level skip / mask decisions
         bool skip = !wave_live;
@@ -322,9 +373,10 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
             }
         }
 
+        const T* ks_ = V1 ? smem + stage * C::K_ELEMS : smem + stage * C::STAGE;
+        const T* vs_ = V1 ? smem + 2 * C::K_ELEMS : ks_ + C::K_ELEMS;
+        float pr[NKB][16];
         if (!skip) {
-            const T* ks_ = smem + stage * C::STAGE;
-            const T* vs_ = ks_ + C::K_ELEMS;
 
             // S^T = K . Q^T
             f32x16 sacc[NKB];
@@ -411,13 +463,18 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
             const float m_sub = (m_ref == -INFINITY) ? 0.f : m_ref;
 
             // level 2 terms: P = 2^(s*c - m_ref); masked entries give 2^-inf = 0
-            float pr[NKB][16];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     pr[kb][j] = fast_exp2(ALIBI ? sacc[kb][j] - m_sub : fmaf(sacc[kb][j], c, -m_sub));
 
+        }
+        if constexpr (V1) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V(t) (and K(t+1)) landed
+            __syncthreads();                     // ... and every other wave's
+        }
+        if (!skip) {
             // level 3: O^T += V^T . P^T (16-bit: the rounded P also feeds l)
             if constexpr (F32) {
 #pragma unroll
@@ -449,7 +506,9 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
             }
         }
 
-        if (t + 1 < ntiles) store_tile(stage ^ 1, k0 + BN);
+        if constexpr (!V1) {
+            if (t + 1 < ntiles) store_tile(stage ^ 1, k0 + BN);
+        }
     }
 
     // ---------------- epilogue: O /= l, lse = ln sum exp
