@@ -55,16 +55,9 @@ struct FwdCfg {
 #ifndef RF_FWD_WAVES_D64
 #define RF_FWD_WAVES_D64 4
 #endif
-// Waves per SIMD of the plain 16-bit D = 128 instance: its single V buffer
-// (see below) lets 3 work-groups share a CU's LDS.
-#ifndef RF_FWD_WAVES_D128
-#define RF_FWD_WAVES_D128 3
-#endif
 
 template <typename T, int D, bool ROPE, bool ALIBI>
-__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64
-                                          : (D == 128 && sizeof(T) == 2 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D128
-                                                                                           : 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
     using C = FwdCfg<T, D, SPLITK>;
     constexpr bool F32 = C::F32;
@@ -79,10 +72,11 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     constexpr float RESCALE_SLACK = 8.0f;  // log2 units
     typedef typename Vec16<T>::type VecT;
     // V1 (16-bit, D = 128, no RoPE or ALiBi): two K buffers and one V buffer
-    // (52 KB, so 3 work-groups fit a CU), both filled by buffer loads that
-    // write LDS directly.  Tile t's V and tile t+1's K are issued together
-    // once every wave has finished tile t-1's P.V; V(t) lands under tile t's
-    // score products and softmax, and a second barrier precedes the P.V.
+    // (52 KB instead of 70), both filled by buffer loads that write LDS
+    // directly, so no registers stage the tiles.  Tile t's V and tile t+1's K
+    // are issued together once every wave has finished tile t-1's P.V; V(t)
+    // lands under tile t's score products and softmax, and a second barrier
+    // precedes the P.V.
     constexpr bool V1 = D == 128 && !F32 && !ROPE && !ALIBI;
 
     __shared__ __attribute__((aligned(16))) T smem[V1 ? 2 * C::K_ELEMS + BN * KS : 2 * C::STAGE];
