@@ -372,8 +372,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards over (batch, head) with no exchange, see the design notes)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported. Prefill shards "
+              "over (batch, head) and decode over (batch, KV head) with no exchange, so each GPU runs "
+              "this one-GPU workload on its share.", file=sys.stderr)
         sys.exit(2)
 
     import torch

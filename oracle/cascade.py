@@ -16,7 +16,7 @@ Sources (cited by page title and the part of the page):
   * "Operator Fusion" guide, section 2, Pattern 4 (scores = Q K^T / sqrt(dk),
     mask, softmax, times V).
 
-Readings where the pages are silent (each is also listed in the design notes):
+Readings where the pages are silent:
   * query row i sits at position p_i = Nk - Nq + i; key row j at position j
     (bottom-right alignment; equals i when Nq == Nk);
   * causal: key j visible iff j <= p_i; sliding window W: p_i - W < j <= p_i;
