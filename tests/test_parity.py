@@ -65,6 +65,11 @@ FWD_CASES = [
     ("bf16", 128, 1, 4, 1, 200, 200, "causal", 0, 10000.0),
     ("bf16", 64, 1, 2, 2, 190, 190, "none", 0, 500.0),
     ("bf16", 128, 1, 2, 2, 64, 64, "none", 0, 0.0),
+    # D = 128 16-bit without RoPE: direct-to-LDS K/V, single V buffer; GQA,
+    # Nq < Nk with bottom-right alignment and ragged tails
+    ("bf16", 128, 2, 4, 2, 190, 333, "causal", 0, 0.0),
+    ("f16", 128, 1, 4, 1, 77, 77, "none", 0, 0.0),
+    ("bf16", 128, 1, 2, 2, 129, 700, "sliding", 200, 0.0),
     # RoPE over many tiles and at large positions (up to 70,000 keys, so
     # angles of thousands of revolutions), with windows starting mid-tile
     ("f16", 64, 1, 2, 2, 64, 2100, "causal", 0, 10000.0),
