@@ -108,6 +108,25 @@ def test_fwd_f16_d64_scale_range_matches_oracle(scale):
         compare(o, lse, ro, rl, TOL["f16"], f"scale {scale} {mask}")
 
 
+@pytest.mark.parametrize("mask", ["causal", "none"])
+def test_fwd_f16_d64_late_dominant_key(mask):
+    """fp16, D = 64: keys far past the first tile whose scores exceed every
+    earlier one by more than 2^16 in the terms (rows of one head only), so the
+    reference taken from a row's first tile no longer holds and the block must
+    be redone with the running max; the result must still match the oracle."""
+    q, k, v = gen_qkv(1, 2, 2, 700, 700, 64, "f16", 6)
+    q = q.float()
+    k = k.float()
+    q[0, 1] = q[0, 1].abs() + 0.5                      # head 1: positive queries
+    k[0, 1, 300] = 4.0                                  # dominant keys at 300 and 650
+    k[0, 1, 650] = 3.0
+    q, k = q.half(), k.half()
+    print(f"case fwd f16 D=64 dominant late keys {mask}", flush=True)
+    o, lse = run_fwd(q, k, v, 0.125, mask, 0, 0.0)
+    ro, rl = oracle.attention(q, k, v, 0.125, mask)
+    compare(o, lse, ro, rl, TOL["f16"], f"late dominant key {mask}")
+
+
 def test_fwd_empty_keys_gives_zero_and_neg_inf():
     q, k, v = gen_qkv(1, 2, 2, 40, 0, 64, "f16", 1)
     o, lse = run_fwd(q, k, v, 0.125, "none", 0, 0.0)
