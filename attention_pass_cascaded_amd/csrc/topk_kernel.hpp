@@ -195,16 +195,20 @@ __global__ __launch_bounds__(TOPK_THREADS) void softmax_topk16_kernel(const T* _
     l = topk_group_sum<LPR>(l);
     const float inv_l = 1.f / l;
 
-    // level 3: k - 1 more rounds; the taken key drops to 0
+    // level 3: k - 1 more rounds.  Keys are unique and the winners come in
+    // decreasing order, so the untaken keys are exactly those below the last
+    // winner: each lane's candidate is its largest key below win, found as
+    // w1 - min(w1, min(w1 - key)) with w1 = win - 1 in wrapping unsigned
+    // arithmetic.  A taken key (>= win) wraps above w1, so a lane with no
+    // untaken key keeps t = w1 and offers 0.  win > 0 in every round since
+    // k <= E and every present key is nonzero.
     unsigned mine = sub == 0 ? win : 0u;
     for (int j = 1; j < k; ++j) {
-        best = 0;
+        const unsigned w1 = win - 1u;
+        unsigned t = w1;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            key[i] = key[i] == win ? 0u : key[i];
-            best = max(best, key[i]);
-        }
-        win = topk_group_max<LPR>(best);
+        for (int i = 0; i < VPL; ++i) t = min(t, w1 - key[i]);
+        win = topk_group_max<LPR>(w1 - t);
         mine = sub == j ? win : mine;
     }
     if (row_ok && sub < k) {
