@@ -123,7 +123,7 @@ __device__ __forceinline__ unsigned topk_unmono16(unsigned m) {
 
 template <int CTRL>
 __device__ __forceinline__ unsigned topk_dpp(unsigned x) {
-    return (unsigned)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1, 0, 3, 2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2, 3, 0, 1]
