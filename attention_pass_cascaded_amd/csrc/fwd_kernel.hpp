@@ -21,6 +21,8 @@
 //   transpose read (ds_read_b64_tr_b16), 4 keys of one d column per lane.
 // K/V tiles are double-buffered: the global loads of tile t+1 are issued
 // before the math of tile t and written to LDS after it (one barrier a tile).
+// 16-bit D = 128 without RoPE or ALiBi instead loads straight into LDS, with
+// two K buffers and one V buffer (two barriers a tile).
 //
 // The O rescale is lazy: the reference max m_ref only moves when a tile's max
 // exceeds it by more than 2^8, so P = 2^(s - m_ref) <= 256 (exact range in
@@ -371,7 +373,6 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         const T* vs_ = V1 ? smem + 2 * C::K_ELEMS : ks_ + C::K_ELEMS;
         float pr[NKB][16];
         if (!skip) {
-
             // S^T = K . Q^T
             f32x16 sacc[NKB];
 #pragma unroll
