@@ -70,6 +70,7 @@ FWD_CASES = [
     ("bf16", 128, 2, 4, 2, 190, 333, "causal", 0, 0.0),
     ("f16", 128, 1, 4, 1, 77, 77, "none", 0, 0.0),
     ("bf16", 128, 1, 2, 2, 129, 700, "sliding", 200, 0.0),
+    ("f16", 128, 1, 2, 1, 150, 100, "causal", 0, 0.0),      # Nq > Nk: the first 50 rows see no key
     # RoPE over many tiles and at large positions (up to 70,000 keys, so
     # angles of thousands of revolutions), with windows starting mid-tile
     ("f16", 64, 1, 2, 2, 64, 2100, "causal", 0, 10000.0),
