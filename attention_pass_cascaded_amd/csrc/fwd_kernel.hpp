@@ -138,7 +138,18 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     int khi = min(p.Nk, klo + p.split_len);
     if (p.mask != RF_MASK_NONE) khi = min(khi, last_row + pos_off + 1);
     if (p.mask == RF_MASK_SLIDING) klo = max(klo, q0 + pos_off - p.window + 1);
+    // Sliding window (one split, direct-to-LDS staging): tiles sit on the
+    // global grid of BN keys and a work-group visits them in the cyclic order
+    // that puts tile j at step j mod ntiles.  Interior query blocks all have
+    // the same tile count, so neighbouring blocks, running side by side on one
+    // XCD, read the tiles they share at the same step and the second read hits
+    // L2.  Keys below klo are outside every row's window and are masked like
+    // any other.  (Other instances keep the plain ascending order and its code.)
+    const bool cyc = V1 && p.mask == RF_MASK_SLIDING && !p.split_mode && khi > klo;
+    if (cyc) klo -= klo % BN;
     const int ntiles = khi > klo ? (khi - klo + BN - 1) / BN : 0;
+    // tile index at step 0, then +1 per step with wrap-around
+    int tcur = cyc ? (ntiles - (klo / BN) % ntiles) % ntiles : 0;
 
     // This wave's rows and their positions.
     const int wrow0 = q0 + 32 * wave;
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
 
     if (ntiles > 0) {
         if constexpr (V1) {
-            issue_rows(krs, smem, klo);
+            issue_rows(krs, smem, klo + tcur * BN);
         } else {
             load_tile(klo);
             store_tile(0, klo);
@@ -346,15 +357,23 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     }
 
     for (int t = 0; t < ntiles; ++t) {
-        const int k0 = klo + t * BN;
+        int k0, k0n;  // this step's tile and the next one's
+        if constexpr (V1) {
+            k0 = klo + tcur * BN;
+            tcur = tcur + 1 == ntiles ? 0 : tcur + 1;
+            k0n = klo + tcur * BN;
+        } else {
+            k0 = klo + t * BN;
+            k0n = k0 + BN;
+        }
         const int stage = t & 1;
         if constexpr (V1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(t) landed
         __syncthreads();
         if constexpr (V1) {
             issue_rows(vrs, smem + 2 * C::K_ELEMS, k0);
-            if (t + 1 < ntiles) issue_rows(krs, smem + (stage ^ 1) * C::K_ELEMS, k0 + BN);
+            if (t + 1 < ntiles) issue_rows(krs, smem + (stage ^ 1) * C::K_ELEMS, k0n);
         } else if (t + 1 < ntiles) {
-            load_tile(k0 + BN);
+            load_tile(k0n);
         }
 
         // wave-level skip / mask decisions
@@ -502,7 +521,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         }
 
         if constexpr (!V1) {
-            if (t + 1 < ntiles) store_tile(stage ^ 1, k0 + BN);
+            if (t + 1 < ntiles) store_tile(stage ^ 1, k0n);
         }
     }
 

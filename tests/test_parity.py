@@ -71,6 +71,10 @@ FWD_CASES = [
     ("f16", 128, 1, 4, 1, 77, 77, "none", 0, 0.0),
     ("bf16", 128, 1, 2, 2, 129, 700, "sliding", 200, 0.0),
     ("f16", 128, 1, 2, 1, 150, 100, "causal", 0, 0.0),      # Nq > Nk: the first 50 rows see no key
+    # D = 128 16-bit sliding window: tiles visited in cyclic order from a
+    # grid-aligned start, with windows that are not tile multiples
+    ("f16", 128, 1, 2, 2, 777, 777, "sliding", 300, 0.0),
+    ("bf16", 128, 1, 3, 1, 400, 1000, "sliding", 97, 0.0),
     # RoPE over many tiles and at large positions (up to 70,000 keys, so
     # angles of thousands of revolutions), with windows starting mid-tile
     ("f16", 64, 1, 2, 2, 64, 2100, "causal", 0, 10000.0),
@@ -126,6 +130,24 @@ def test_fwd_f16_d64_late_dominant_key(mask):
     o, lse = run_fwd(q, k, v, 0.125, mask, 0, 0.0)
     ro, rl = oracle.attention(q, k, v, 0.125, mask)
     compare(o, lse, ro, rl, TOL["f16"], f"late dominant key {mask}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fwd_d128_sliding_dominant_keys(dt):
+    """D = 128 sliding window: a dominant key inside each row's window, at
+    different offsets from the tile the work-group visits first, so the
+    running max must move mid-row whatever the visiting order."""
+    q, k, v = gen_qkv(1, 2, 2, 600, 600, 128, dt, 8)
+    q = q.float()
+    k = k.float()
+    q[0, 1] = q[0, 1].abs() + 0.5
+    for j in (100, 230, 390, 520):
+        k[0, 1, j] = 3.0
+    q, k = q.to(v.dtype), k.to(v.dtype)
+    print(f"case fwd {dt} D=128 sliding dominant keys", flush=True)
+    o, lse = run_fwd(q, k, v, 1 / math.sqrt(128), "sliding", 200, 0.0)
+    ro, rl = oracle.attention(q, k, v, 1 / math.sqrt(128), "sliding", 200)
+    compare(o, lse, ro, rl, TOL[dt], f"sliding dominant keys {dt}")
 
 
 def test_fwd_empty_keys_gives_zero_and_neg_inf():
