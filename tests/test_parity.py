@@ -75,6 +75,8 @@ FWD_CASES = [
     # grid-aligned start, with windows that are not tile multiples
     ("f16", 128, 1, 2, 2, 777, 777, "sliding", 300, 0.0),
     ("bf16", 128, 1, 3, 1, 400, 1000, "sliding", 97, 0.0),
+    ("f16", 128, 1, 2, 2, 1, 300, "sliding", 50, 0.0),       # one query row at position 299
+    ("bf16", 128, 1, 2, 1, 200, 200, "sliding", 5000, 0.0),  # window wider than the sequence
     # RoPE over many tiles and at large positions (up to 70,000 keys, so
     # angles of thousands of revolutions), with windows starting mid-tile
     ("f16", 64, 1, 2, 2, 64, 2100, "causal", 0, 10000.0),
