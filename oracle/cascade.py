@@ -347,16 +347,68 @@ def lse_merge(o_parts, lse_parts):
     return O, lse
 
 
+# --------------------------------------------------------------------------
+# Output rounding: what a kernel that rounds the exact result once would err
+# --------------------------------------------------------------------------
+def round_to(o64, dtype) -> np.ndarray:
+    """rn_dtype(O): the float64 values rounded once, to nearest even, to ``dtype``
+    (a torch dtype), returned as float64."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(_f64(o64)))
+    return t.to(dtype).to(torch.float64).numpy()
+
+
 def rounding_floor(o64: np.ndarray, dtype) -> float:
     """max |rn_dtype(O) - O|: the error that rounding the exact output alone makes."""
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(o64))
-    r = t.to(dtype).to(torch.float64)
-    return float((r - t).abs().max()) if t.numel() else 0.0
+    o64 = _f64(o64)
+    return float(np.abs(round_to(o64, dtype) - o64).max()) if o64.size else 0.0
+
+
+# significand bits (hidden bit included) and exponent of the smallest normal
+_FORMAT = {"float16": (11, -14), "bfloat16": (8, -126), "float32": (24, -126)}
+
+
+def output_ulp(x, dtype) -> np.ndarray:
+    """Spacing of ``dtype``'s grid at each value of x (values of that grid, as
+    float64): 2^(e - p + 1) for |x| in [2^e, 2^(e+1)) with p significand bits,
+    and the subnormal spacing below the smallest normal."""
+    name = str(dtype).replace("torch.", "")
+    p, emin = _FORMAT[name]
+    a = np.abs(_f64(x))
+    _, e = np.frexp(np.where(a > 0, a, 1.0))   # a = m 2^e, m in [0.5, 1)
+    e = np.maximum(e - 1, emin)
+    return np.ldexp(1.0, e - p + 1)
+
+
+def error_report(o, lse, o64, lse64, dtype) -> dict:
+    """Error of a kernel's (o, lse) against the exact (o64, lse64).
+
+    max_abs_o / max_abs_lse: max |o - O|, max |lse - LSE| over finite LSE;
+    floor: max |rn(O) - O|, what rounding the exact output once costs;
+    ulps: max |o - rn(O)| in spacings of the output grid at the largest
+    |rn(O)| of the element's row (0 for a kernel whose only error is that one
+    rounding; the row's scale, since an element near zero has a grid far
+    finer than the row's accumulation error); worst: index and values of the
+    element with the largest |o - O|.
+    """
+    o, lse, o64, lse64 = _f64(o), _f64(lse), _f64(o64), _f64(lse64)
+    rn = round_to(o64, dtype)
+    row_scale = np.abs(rn).max(axis=-1, keepdims=True) if rn.size else rn
+    d = np.abs(o - o64)
+    fin = np.isfinite(lse64)
+    at = np.unravel_index(int(np.argmax(d)), d.shape) if d.size else ()
+    return {
+        "max_abs_o": float(d.max()) if d.size else 0.0,
+        "max_abs_lse": float(np.abs(lse[fin] - lse64[fin]).max()) if fin.any() else 0.0,
+        "floor": float(np.abs(rn - o64).max()) if o64.size else 0.0,
+        "ulps": float((np.abs(o - rn) / output_ulp(row_scale, dtype)).max()) if o64.size else 0.0,
+        "worst": {"index": [int(i) for i in at], "o": float(o[at]) if d.size else 0.0,
+                  "o_exact": float(o64[at]) if d.size else 0.0},
+    }
 
 
 __all__ = [
     "attention", "attention_rows", "attention_incremental", "split_partials",
     "split_bounds", "lse_merge", "rope_rotate", "visible_mask", "query_positions",
-    "softmax_probs", "rounding_floor", "alibi_bias",
+    "softmax_probs", "rounding_floor", "round_to", "output_ulp", "error_report", "alibi_bias",
 ]

@@ -156,6 +156,84 @@ def test_split_bounds_cover_keys_once():
             assert all(hi - lo == 512 for lo, hi in b)
 
 
+@pytest.mark.parametrize("Nk,S,bounds", [
+    # chunk c covers [c*ceil(Nk/S), min(Nk, (c+1)*ceil(Nk/S))), worked by hand:
+    # ceil(100/7) = 15, so six full chunks and a short last one [90, 100)
+    (100, 7, [(0, 15), (15, 30), (30, 45), (45, 60), (60, 75), (75, 90), (90, 100)]),
+    # ceil(5/8) = 1: one key per chunk, the last three chunks empty
+    (5, 8, [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 5), (6, 6), (7, 7)]),
+    # ceil(10/4) = 3: a floor split (2, 2, 3, 3 or 3, 3, 2, 2) would differ
+    (10, 4, [(0, 3), (3, 6), (6, 9), (9, 10)]),
+    # ceil(7/3) = 3, and a chunk that starts exactly at Nk
+    (6, 4, [(0, 2), (2, 4), (4, 6), (6, 6)]),
+    (1, 3, [(0, 1), (1, 1), (2, 2)]),
+])
+def test_split_bounds_hand_cases(Nk, S, bounds):
+    # compared as the keys each chunk holds (an empty chunk may be written
+    # [lo, hi) with lo >= hi)
+    got = [list(range(lo, hi)) for lo, hi in A.split_bounds(Nk, S)]
+    assert got == [list(range(lo, hi)) for lo, hi in bounds]
+    assert [lo for lo, _ in A.split_bounds(Nk, S)] == [lo for lo, _ in bounds]
+
+
+# ------------------------------------------------- output rounding and ulps
+F16_CASES = [
+    # (exact value, its fp16 rounding worked by hand with ties to even)
+    (1.0 + 2.0 ** -12, 1.0),                      # grid 2^-10 on [1, 2): a quarter spacing rounds down
+    (1.0 + 3 * 2.0 ** -12, 1.0 + 2.0 ** -10),     # nearest is 1+2^-10 (distance 2^-12)
+    (1.0 + 2.0 ** -11, 1.0),                      # exact tie between 1 and 1+2^-10 -> even 1.0
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2 * 2.0 ** -10),  # tie between 1+2^-10 (odd) and 1+2^-9 -> 1+2^-9
+    (2049.0, 2048.0),                             # spacing 2 above 2048: tie -> even 2048
+    (2051.0, 2052.0),                             # tie between 2050 (odd) and 2052 -> 2052
+    (-0.3, -1229 * 2.0 ** -12),                   # 0.3 in [0.25, 0.5): spacing 2^-12, 0.3 = 1228.8 spacings
+]
+
+
+def test_round_to_fp16_hand_cases():
+    x = np.array([c[0] for c in F16_CASES])
+    assert np.array_equal(A.round_to(x, torch.float16), np.array([c[1] for c in F16_CASES]))
+
+
+def test_rounding_floor_hand_cases():
+    # the floor is the largest |rn(x) - x| over the array
+    assert A.rounding_floor(np.array([1.0 + 2.0 ** -12, 0.5, 1.0]), torch.float16) == 2.0 ** -12
+    assert A.rounding_floor(np.array([2049.0, 1.0 + 2.0 ** -12]), torch.float16) == 1.0
+    # bf16 keeps 8 significand bits: spacing 2^-7 on [1, 2); 1 + 2^-8 is a tie -> 1.0
+    assert A.rounding_floor(np.array([1.0 + 2.0 ** -8]), torch.bfloat16) == 2.0 ** -8
+    assert A.rounding_floor(np.array([3.0 + 2.0 ** -9]), torch.bfloat16) == 2.0 ** -9  # spacing 2^-6 on [2, 4)
+    assert A.rounding_floor(np.array([0.25, -4.0, 0.0]), torch.bfloat16) == 0.0        # on the grid
+    assert A.rounding_floor(np.zeros(0), torch.float16) == 0.0
+
+
+def test_output_ulp_matches_library_spacing():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(2000) * 4.0, [1.0, 2.0, 0.75, 2048.0, 2.0 ** -20, 2.0 ** -14, 6e4]])
+    h = v.astype(np.float16)
+    assert np.array_equal(A.output_ulp(h.astype(np.float64), torch.float16), np.spacing(np.abs(h)).astype(np.float64))
+    bt = torch.tensor(v, dtype=torch.bfloat16).abs()
+    ref = (torch.nextafter(bt, torch.full_like(bt, float("inf"))) - bt).to(torch.float64).numpy()
+    assert np.array_equal(A.output_ulp(bt.to(torch.float64).numpy(), torch.bfloat16), ref)
+    f = v.astype(np.float32)
+    assert np.array_equal(A.output_ulp(f.astype(np.float64), torch.float32), np.spacing(np.abs(f)).astype(np.float64))
+
+
+def test_error_report_hand_case():
+    o64 = np.array([[1.0 + 2.0 ** -12, 0.5], [2049.0, -1.0]])
+    lse64 = np.array([0.5, -np.inf])
+    # a kernel that rounds once is 0 ulps off rn(O); one more spacing is 1 ulp
+    o = A.round_to(o64, torch.float16)
+    r = A.error_report(o, np.array([0.5 + 1e-4, -np.inf]), o64, lse64, torch.float16)
+    assert r["ulps"] == 0.0 and r["floor"] == 1.0 and r["max_abs_o"] == 1.0
+    assert r["max_abs_lse"] == pytest.approx(1e-4) and r["worst"]["index"] == [1, 0]
+    o[0, 1] = 0.5 + 2.0 ** -10   # one fp16 spacing of the row's largest |O| (1.0) above 0.5
+    assert A.error_report(o, lse64, o64, lse64, torch.float16)["ulps"] == 1.0
+    # an element near zero is measured on its row's scale, not its own grid
+    o64 = np.array([[2.0 ** -20, 1.0]])
+    o = A.round_to(o64, torch.float16)
+    o[0, 0] += 2.0 ** -12        # a quarter spacing at 1.0, 2^12 spacings at 2^-20
+    assert A.error_report(o, np.zeros(1), o64, np.zeros(1), torch.float16)["ulps"] == 0.25
+
+
 # ---------------------------------------------------------------- closed forms
 def test_single_key():
     q, k, v = rnd((1, 2, 4, 8), 50), rnd((1, 2, 1, 8), 51), rnd((1, 2, 1, 8), 52)
@@ -346,3 +424,32 @@ def test_alibi_zero_slope_is_plain_attention_and_matches_sdpa():
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.3)
     close(o2, ref.numpy(), rtol=1e-11, atol=1e-13)
+
+
+# ------------------------------------------- whole-output report (oracle/report.py)
+def test_compare_full_reports_rounding_only_and_finds_a_planted_error():
+    from oracle import report
+    q, k, v = (t for t in __import__("workloads").gen_qkv(2, 4, 2, 40, 40, 8, torch.float16, 21))
+    o64, l64 = oracle.attention(q, k, v, 0.3, "causal")
+    o = torch.from_numpy(o64).to(torch.float16)         # the exact result rounded once
+    lse = torch.from_numpy(l64).to(torch.float32)
+    r = report.compare_full(q, k, v, o, lse, 0.3, "causal", 0, 0.0, torch.float16)
+    assert r["ulps"] == 0.0 and r["max_abs_o"] == r["floor"] > 0
+    assert r["max_abs_lse"] < 1e-6
+    o[1, 3, 17, 5] += 0.25                              # one wrong element in head 3 (KV group 1)
+    lse[0, 2, 9] = 7.0
+    r = report.compare_full(q, k, v, o, lse, 0.3, "causal", 0, 0.0, torch.float16)
+    assert r["worst"]["index"] == [1, 3, 17, 5] and r["max_abs_o"] > 0.2
+    assert r["max_abs_lse"] == pytest.approx(abs(7.0 - l64[0, 2, 9]), rel=1e-6)
+    lse[0, 2, 9] = -float("inf")                        # a -inf where a key is visible
+    assert report.compare_full(q, k, v, o, lse, 0.3, "causal", 0, 0.0, torch.float16)["max_abs_lse"] == float("inf")
+
+
+def test_compare_partials_against_merge():
+    from oracle import report
+    q, k, v = (t for t in __import__("workloads").gen_qkv(1, 4, 2, 1, 50, 8, torch.float32, 22))
+    op, lp = oracle.split_partials(q, k, v, 0.5, 4)
+    assert report.compare_partials(q, k, v, torch.from_numpy(op), torch.from_numpy(lp), 0.5, 4) == (0.0, 0.0)
+    op[0, 1, 0, 2, 3] += 1e-3
+    e_o, e_l = report.compare_partials(q, k, v, torch.from_numpy(op), torch.from_numpy(lp), 0.5, 4)
+    assert e_o == pytest.approx(1e-3) and e_l == 0.0
