@@ -1,8 +1,10 @@
 """ctypes binding to librfattn.so, with the same entry points as include/rf_attn.h.
 
-This layer only marshals arguments: it checks tensor placement, dtype and
-contiguity, allocates outputs with torch on the input's device, and passes raw
-device pointers plus the current HIP stream.  Every step of the computation
+This layer only marshals arguments: it checks the placement, dtype, shape and
+contiguity of every tensor it hands over (inputs and caller-provided output
+buffers alike, so that no kernel writes past a buffer that is too small),
+allocates the outputs the caller does not provide with torch on the input's
+device, and passes raw device pointers plus the current HIP stream.  Every step of the computation
 runs in the HIP kernels.  There is no fallback: if the library is missing or a
 call fails, an exception is raised.
 """
@@ -22,7 +24,7 @@ _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
 EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
-            "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_attn_bwd",
+            "rf_splitkv_num_splits", "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_attn_bwd",
             "rf_attn_bwd_workspace_bytes", "rf_layernorm_fwd", "rf_softmax_topk", "rf_status_string",
             "rf_last_error")
 
@@ -54,6 +56,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_attn_fwd_alibi.restype = i
     lib.rf_attn_splitkv_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, f, vp, i, i, vp]
     lib.rf_attn_splitkv_fwd_alibi.restype = i
+    lib.rf_splitkv_num_splits.argtypes = [i, i, i, i]
+    lib.rf_splitkv_num_splits.restype = i
     lib.rf_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.rf_splitkv_workspace_bytes.restype = sz
     lib.rf_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
@@ -107,6 +111,25 @@ def _check_inputs(q, k, v):
     return B, Hq, k.shape[1], Nq, k.shape[2], D
 
 
+def _out(name, t, shape, dtype, device):
+    """A caller-provided output buffer: allocate it when absent, else check that
+    it is a contiguous tensor of exactly ``shape`` and ``dtype`` on ``device``."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != torch.device(device):  # the inputs it goes with are already on the GPU
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
 def _scale(scale, D):
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
@@ -144,16 +167,23 @@ def fwd(q, k, v, scale=None, mask="none", window=0, rope_base=0.0, out=None, lse
             return fwd_prerotated(q, k, v, rope_base, scale=scale, mask=mask, window=window, out=out,
                                   lse=lse, alibi_slopes=alibi_slopes)
     B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _out("out", out, q.shape, q.dtype, q.device)
+    lse = _out("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     slopes = _slopes(alibi_slopes, Hq, q.device)
     lib = load_library()
     _check(lib.rf_attn_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, D,
                                  _scale(scale, D), _MASK[mask], int(window), float(rope_base), _ptr(slopes),
                                  _DTYPE[q.dtype], _stream(q)))
     return out, lse
+
+
+def num_splits_for(q, k, cu_count: int = 0) -> int:
+    """The library's chunk count (rf_splitkv_num_splits) for q [B,Hq,Nq,D]
+    against k [B,Hkv,Nk,D]; cu_count 0 asks the current device."""
+    n = int(load_library().rf_splitkv_num_splits(k.shape[0], k.shape[1], k.shape[2], int(cu_count)))
+    if n < 1:
+        raise ValueError("invalid sizes for a split-KV call")
+    return n
 
 
 def workspace_bytes(B, Hq, Nq, D, num_splits) -> int:
@@ -165,10 +195,8 @@ def splitkv_fwd(q, k, v, num_splits, scale=None, mask="none", window=0, rope_bas
     """Split-KV partials: (o_part [B,Hq,Nq,S,D] float32, lse_part [B,Hq,Nq,S] float32)."""
     B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
     S = int(num_splits)
-    if o_part is None:
-        o_part = torch.empty((B, Hq, Nq, S, D), dtype=torch.float32, device=q.device)
-    if lse_part is None:
-        lse_part = torch.empty((B, Hq, Nq, S), dtype=torch.float32, device=q.device)
+    o_part = _out("o_part", o_part, (B, Hq, Nq, S, D), torch.float32, q.device)
+    lse_part = _out("lse_part", lse_part, (B, Hq, Nq, S), torch.float32, q.device)
     slopes = _slopes(alibi_slopes, Hq, q.device)
     lib = load_library()
     _check(lib.rf_attn_splitkv_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part),
@@ -188,10 +216,14 @@ def lse_merge(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
     if tuple(lse_part.shape) != lead + (S,):
         raise ValueError("lse_part must be o_part.shape[:-1]")
     rows = math.prod(lead)
-    if out is None:
-        out = torch.empty(lead + (D,), dtype=out_dtype, device=o_part.device)
-    if lse is None:
-        lse = torch.empty(lead, dtype=torch.float32, device=o_part.device)
+    if lse_part.device != o_part.device:
+        raise ValueError("o_part and lse_part must be on one device")
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in _DTYPE:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    out = _out("out", out, lead + (D,), out_dtype, o_part.device)
+    lse = _out("lse", lse, lead, torch.float32, o_part.device)
     lib = load_library()
     _check(lib.rf_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), rows, S, D,
                             _DTYPE[out.dtype], _stream(o_part)))
@@ -202,8 +234,7 @@ def rope_rotate(x, base, pos_offset=0, out=None):
     """Rotary embedding of x [B, H, N, D] at positions pos_offset + n (out may be x)."""
     if not x.is_cuda or x.dim() != 4 or not x.is_contiguous() or x.dtype not in _DTYPE:
         raise ValueError("x must be a contiguous [B, H, N, D] GPU tensor of float32/float16/bfloat16")
-    if out is None:
-        out = torch.empty_like(x)
+    out = _out("out", out, x.shape, x.dtype, x.device)
     B, H, N, D = x.shape
     _check(load_library().rf_rope_rotate(_ptr(x), _ptr(out), B * H, N, D, float(base), int(pos_offset),
                                          _DTYPE[x.dtype], _stream(x)))
@@ -220,8 +251,11 @@ def fwd_prerotated(q, k, v, rope_base, scale=None, mask="none", window=0, out=No
                alibi_slopes=alibi_slopes)
 
 
-def decode(q, k, v, num_splits=64, scale=None, mask="none", window=0, rope_base=0.0, alibi_slopes=None):
-    """Split-KV attention: partials then log-sum-exp merge.  Returns (o, lse) like fwd."""
+def decode(q, k, v, num_splits=None, scale=None, mask="none", window=0, rope_base=0.0, alibi_slopes=None):
+    """Split-KV attention: partials then log-sum-exp merge.  Returns (o, lse)
+    like fwd.  num_splits None takes the library's rule (num_splits_for)."""
+    if num_splits is None:
+        num_splits = num_splits_for(q, k)
     op, lp = splitkv_fwd(q, k, v, num_splits, scale, mask, window, rope_base, alibi_slopes=alibi_slopes)
     return lse_merge(op, lp, out_dtype=q.dtype)
 
@@ -236,13 +270,16 @@ def bwd(q, k, v, o, lse, dout, scale=None, mask="none", window=0, rope_base=0.0,
             raise ValueError(f"{name} must be a contiguous GPU tensor like q")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = _out("dq", dq, q.shape, q.dtype, q.device)
+    dk = _out("dk", dk, k.shape, k.dtype, q.device)
+    dv = _out("dv", dv, v.shape, v.dtype, q.device)
     lib = load_library()
+    nbytes = int(lib.rf_attn_bwd_workspace_bytes(B, Hq, Nq))
     if workspace is None:
-        nbytes = int(lib.rf_attn_bwd_workspace_bytes(B, Hq, Nq))
         workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    elif (not workspace.is_cuda or workspace.device != q.device or workspace.dtype != torch.float32
+          or not workspace.is_contiguous() or workspace.numel() * 4 < nbytes):
+        raise ValueError(f"workspace must be a contiguous float32 tensor on {q.device} of at least {nbytes} bytes")
     slopes = _slopes(alibi_slopes, Hq, q.device)
     _check(lib.rf_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                            _ptr(dv), _ptr(workspace), B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask],
@@ -259,9 +296,9 @@ def layernorm(x, gamma, beta, eps=1e-5, y=None, mean=None, rstd=None):
         if not t.is_cuda or t.dtype != x.dtype or tuple(t.shape) != (H,) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [H] GPU tensor of x's dtype")
     rows = x.numel() // H if H else 0
-    y = torch.empty_like(x) if y is None else y
-    mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if mean is None else mean
-    rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if rstd is None else rstd
+    y = _out("y", y, x.shape, x.dtype, x.device)
+    mean = _out("mean", mean, x.shape[:-1], torch.float32, x.device)
+    rstd = _out("rstd", rstd, x.shape[:-1], torch.float32, x.device)
     _check(load_library().rf_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd),
                                            rows, H, float(eps), _DTYPE[x.dtype], _stream(x)))
     return y, mean, rstd
@@ -275,8 +312,8 @@ def softmax_topk(x, k, values=None, indices=None):
     E = x.shape[-1]
     rows = x.numel() // E if E else 0
     shape = tuple(x.shape[:-1]) + (int(k),)
-    values = torch.empty(shape, dtype=torch.float32, device=x.device) if values is None else values
-    indices = torch.empty(shape, dtype=torch.int32, device=x.device) if indices is None else indices
+    values = _out("values", values, shape, torch.float32, x.device)
+    indices = _out("indices", indices, shape, torch.int32, x.device)
     _check(load_library().rf_softmax_topk(_ptr(x), _ptr(values), _ptr(indices), rows, E, int(k),
                                           _DTYPE[x.dtype], _stream(x)))
     return values, indices

@@ -172,3 +172,56 @@ def test_softmax_topk_rejects_bad_arguments(lib):
     assert lib.rf_softmax_topk(FAKE, FAKE, FAKE, 4, 2048, 8, 2, None) == B.RF_ERR_UNSUPPORTED   # E
     assert lib.rf_softmax_topk(FAKE, None, FAKE, 4, 256, 8, 2, None) == B.RF_ERR_INVALID_ARG
     assert lib.rf_softmax_topk(None, None, None, 0, 256, 8, 2, None) == B.RF_OK
+
+
+# ---------------------------------------------------------------------------
+# The binding checks every caller-provided output buffer before a pointer
+# reaches the C ABI (a buffer of the wrong shape or dtype would otherwise be
+# written past its end by the kernels).
+# ---------------------------------------------------------------------------
+import torch
+
+
+def test_out_buffer_allocated_when_absent():
+    t = B._out("out", None, (2, 3), torch.float32, "cpu")
+    assert t.shape == (2, 3) and t.dtype == torch.float32 and t.is_contiguous()
+
+
+def test_out_buffer_accepted_when_exact():
+    t = torch.empty(4, 5, dtype=torch.float16)
+    assert B._out("out", t, (4, 5), torch.float16, "cpu") is t
+
+
+@pytest.mark.parametrize("t,needle", [
+    (torch.empty(4, 5, dtype=torch.float32), "float16"),      # wrong dtype
+    (torch.empty(4, 4, dtype=torch.float16), "shape"),        # too small
+    (torch.empty(4, 6, dtype=torch.float16), "shape"),        # too large is refused as well
+    (torch.empty(5, 4, dtype=torch.float16).t(), "contiguous"),
+    (torch.empty(20, dtype=torch.float16), "shape"),          # right size, wrong shape
+    ("not a tensor", "tensor"),
+])
+def test_out_buffer_rejected(t, needle):
+    with pytest.raises(ValueError, match=needle):
+        B._out("out", t, (4, 5), torch.float16, "cpu")
+
+
+def test_out_buffer_on_another_device_rejected():
+    with pytest.raises(ValueError, match="must be on"):
+        B._out("out", torch.empty(4, 5, dtype=torch.float16, device="meta"), (4, 5), torch.float16, "cpu")
+
+
+@pytest.mark.parametrize("B,Hkv,Nk,cu,want", [
+    (16, 8, 32768, 256, 8),      # ceil(4*256 / 128) = 8 chunks of 4096
+    (1, 8, 32768, 256, 128),     # ceil(1024 / 8) = 128, chunks of exactly 256 keys
+    (1, 8, 4096, 256, 16),       # 128 wanted, capped at ceil(4096 / 256) = 16
+    (1, 8, 4097, 256, 17),       # the cap rounds up
+    (16, 8, 16384, 256, 8),
+    (1, 1, 10, 256, 1),          # fewer keys than one chunk's minimum
+    (3, 1, 0, 256, 1),           # no keys: one (empty) chunk
+    (1, 1, 1 << 30, 100000, 4096),  # clamped to the ABI's maximum
+    (0, 8, 4096, 256, 0),        # invalid sizes
+    (1, 0, 4096, 256, 0),
+    (1, 8, -1, 256, 0),
+])
+def test_num_splits_rule(lib, B, Hkv, Nk, cu, want):
+    assert lib.rf_splitkv_num_splits(B, Hkv, Nk, cu) == want

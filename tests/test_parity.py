@@ -330,3 +330,45 @@ def test_rope_mode_auto_switches_above_crossover():
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q, k, v, 0.125, "causal", rope_base=10000.0)
     compare(o, lse, ro, rl, TOL["f16"], "auto rope")
+
+
+# ---------------------------------------------------------------------------
+# A caller-provided output buffer of the wrong shape, dtype or layout is
+# refused by the binding before any pointer reaches a kernel.
+# ---------------------------------------------------------------------------
+def _bad_buffer_calls():
+    dev = torch.device("cuda")
+    q, k, v = (t.to(dev) for t in gen_qkv(1, 4, 2, 8, 40, 64, torch.float16, 11))
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_part_s3 = torch.empty(1, 4, 8, 3, 64, **f32)
+    lse_part_s3 = torch.empty(1, 4, 8, 3, **f32)
+    o, lse = rf.fwd(q, k, v, mask="causal")
+    dout = torch.randn_like(o)
+    x = torch.randn(6, 64, device=dev, dtype=torch.float16)
+    gamma, beta = torch.ones(64, device=dev, dtype=torch.float16), torch.zeros(64, device=dev, dtype=torch.float16)
+    return [
+        ("fwd out dtype", lambda: rf.fwd(q, k, v, out=torch.empty(q.shape, **f32))),
+        ("fwd out too small", lambda: rf.fwd(q, k, v, out=torch.empty(1, 4, 7, 64, dtype=q.dtype, device=dev))),
+        ("fwd lse dtype", lambda: rf.fwd(q, k, v, lse=torch.empty(1, 4, 8, dtype=torch.float16, device=dev))),
+        ("fwd out transposed", lambda: rf.fwd(q, k, v, out=torch.empty(1, 4, 64, 8, dtype=q.dtype, device=dev).transpose(2, 3))),
+        ("split o_part for 3 chunks", lambda: rf.splitkv_fwd(q, k, v, 4, o_part=o_part_s3)),
+        ("split lse_part for 3 chunks", lambda: rf.splitkv_fwd(q, k, v, 4, lse_part=lse_part_s3)),
+        ("merge out shape", lambda: rf.lse_merge(o_part_s3, lse_part_s3, out=torch.empty(1, 4, 8, 32, dtype=q.dtype, device=dev))),
+        ("merge lse dtype", lambda: rf.lse_merge(o_part_s3, lse_part_s3, lse=torch.empty(1, 4, 8, dtype=torch.float64, device=dev))),
+        ("bwd dk shape", lambda: rf.bwd(q, k, v, o, lse, dout, mask="causal", dk=torch.empty_like(q))),
+        ("bwd dq dtype", lambda: rf.bwd(q, k, v, o, lse, dout, mask="causal", dq=torch.empty(q.shape, **f32))),
+        ("bwd workspace small", lambda: rf.bwd(q, k, v, o, lse, dout, mask="causal", workspace=torch.empty(8, **f32))),
+        ("rope out dtype", lambda: rf.rope_rotate(q, 10000.0, out=torch.empty(q.shape, **f32))),
+        ("layernorm mean shape", lambda: rf.layernorm(x, gamma, beta, mean=torch.empty(5, **f32))),
+        ("topk indices dtype", lambda: rf.softmax_topk(x, 4, indices=torch.empty(6, 4, dtype=torch.int64, device=dev))),
+    ]
+
+
+def test_wrong_output_buffers_are_refused():
+    calls = _bad_buffer_calls()
+    torch.cuda.synchronize()
+    for what, call in calls:
+        print(f"wrong buffer: {what}", flush=True)
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
