@@ -18,9 +18,10 @@ from ._binding import (  # noqa: F401
     rope_rotate,
     load_library,
     lse_merge,
+    num_splits_for,
     splitkv_fwd,
     workspace_bytes,
 )
 
-__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "softmax_topk", "workspace_bytes", "load_library",
+__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "softmax_topk", "workspace_bytes", "num_splits_for", "load_library",
            "RFError", "LIB_PATH", "EXPORTED"]

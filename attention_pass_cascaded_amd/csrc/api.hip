@@ -148,6 +148,18 @@ rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                              nullptr, dtype, stream);
 }
 
+int rf_splitkv_num_splits(int B, int Hkv, int Nk, int cu_count) {
+    if (B < 1 || Hkv < 1 || Nk < 0) return 0;
+    if (cu_count <= 0) cu_count = device_cu_count();
+    if (cu_count <= 0) cu_count = 256;
+    const long long heads = (long long)B * Hkv;
+    long long s = ((long long)RF_SPLIT_GROUPS_PER_CU * cu_count + heads - 1) / heads;
+    const long long cap = ((long long)Nk + RF_SPLIT_MIN_KEYS - 1) / RF_SPLIT_MIN_KEYS;
+    if (s > cap) s = cap;
+    if (s > 4096) s = 4096;
+    return s < 1 ? 1 : (int)s;
+}
+
 size_t rf_splitkv_workspace_bytes(int B, int Hq, int Nq, int D, int num_splits) {
     if (B < 0 || Hq < 1 || Nq < 0 || D < 1 || num_splits < 1) return 0;
     return (size_t)B * Hq * Nq * num_splits * (size_t)(D + 1) * sizeof(float);

@@ -210,12 +210,12 @@ __global__ __launch_bounds__(FWD_THREADS, D == 64 ? RF_BWD_DQ_WAVES : 1) void at
                 row = u / CPR;
                 ch = u % CPR;
             }
-            kreg[it] = buf_load16(krs, ((k0 + row) * D + ch * EPC) * (int)sizeof(T));
+            kreg[it] = buf_load16(krs, ((unsigned)(k0 + row) * D + ch * EPC) * (unsigned)sizeof(T));
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
             const int u = it * FWD_THREADS + tid;
-            vreg[it] = buf_load16(vrs, ((k0 + u / CPR) * D + (u % CPR) * EPC) * (int)sizeof(T));
+            vreg[it] = buf_load16(vrs, ((unsigned)(k0 + u / CPR) * D + (u % CPR) * EPC) * (unsigned)sizeof(T));
         }
     };
     auto store_tile = [&](int stage, int k0) {
@@ -515,12 +515,12 @@ __global__ __launch_bounds__(BWD_THREADS, D == 64 ? RF_BWD_KV_WAVES : 1) void at
                 row = u / CPR;
                 ch = u % CPR;
             }
-            qreg[i] = buf_load16(qrs, ((q0 + row) * D + ch * EPC) * (int)sizeof(T));
+            qreg[i] = buf_load16(qrs, ((unsigned)(q0 + row) * D + ch * EPC) * (unsigned)sizeof(T));
         }
 #pragma unroll
         for (int i = 0; i < C::CH; ++i) {
             const int u = i * BWD_THREADS + tid;
-            dreg[i] = buf_load16(drs, ((q0 + u / CPR) * D + (u % CPR) * EPC) * (int)sizeof(T));
+            dreg[i] = buf_load16(drs, ((unsigned)(q0 + u / CPR) * D + (u % CPR) * EPC) * (unsigned)sizeof(T));
         }
         const int r = tid % BQ;
         const bool in = q0 + r < p.Nq;

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
             const int key = k0 + 16 * kgp + n;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                ka[kgp][ks] = __builtin_bit_cast(VecT, buf_load16(rs, (key * D + 32 * ks + 8 * q) * (int)sizeof(T)));
+                ka[kgp][ks] = __builtin_bit_cast(VecT, buf_load16(rs, ((unsigned)key * D + 32 * ks + 8 * q) * (unsigned)sizeof(T)));
         }
     };
     auto load_v = [&](int k0, bool live) {
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(DM_THREADS) void attn_decode_mfma_kernel(AttnParams
 #pragma unroll
         for (int it = 0; it < VLD; ++it) {
             const int u = it * 64 + lane;
-            vr[it] = buf_load16(rs, ((k0 + u / CPR) * D + (u % CPR) * 8) * (int)sizeof(T));
+            vr[it] = buf_load16(rs, ((unsigned)(k0 + u / CPR) * D + (u % CPR) * 8) * (unsigned)sizeof(T));
         }
     };
     constexpr int STRIDE = DM_SUB * DM_WAVES;

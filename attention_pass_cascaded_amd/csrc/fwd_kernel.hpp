@@ -275,12 +275,12 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
                 row = u / CPR;
                 ch = u % CPR;
             }
-            kreg[it] = buf_load16(krs, ((k0 + row) * D + ch * EPC) * (int)sizeof(T));
+            kreg[it] = buf_load16(krs, ((unsigned)(k0 + row) * D + ch * EPC) * (unsigned)sizeof(T));
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
             const int u = it * FWD_THREADS + tid;
-            vreg[it] = buf_load16(vrs, ((k0 + u / CPR) * D + (u % CPR) * EPC) * (int)sizeof(T));
+            vreg[it] = buf_load16(vrs, ((unsigned)(k0 + u / CPR) * D + (u % CPR) * EPC) * (unsigned)sizeof(T));
         }
     };
 

@@ -98,8 +98,10 @@ def traffic_from_profiles(kind: str, workload: str):
 CLOCK_WARM_S = 0.3  # untimed run-in before the warmup steps: lets the GPU clock settle
 
 
-def time_loop(fn, steps: int, warmup: int) -> float:
-    """ms per call: a clock run-in, `warmup` untimed calls, then `steps` timed calls."""
+def time_steps(fn, steps: int, warmup: int) -> dict:
+    """Per-call times in ms: a clock run-in, `warmup` untimed calls, then
+    `steps` calls back to back with an event recorded between consecutive
+    calls on the current stream.  Returns mean (total / steps), median, min."""
     import torch
     t_end = time.perf_counter() + CLOCK_WARM_S
     while time.perf_counter() < t_end:
@@ -109,28 +111,38 @@ def time_loop(fn, steps: int, warmup: int) -> float:
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    end.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": median, "min": per[0]}
 
 
-def run_prefill(w, steps, warmup):
+def time_loop(fn, steps: int, warmup: int) -> float:
+    """Mean ms per call (see time_steps)."""
+    return time_steps(fn, steps, warmup)["mean"]
+
+
+def run_prefill(w, steps, warmup, alibi=False):
     import torch
     import attention_pass_cascaded_amd as rf
-    from workloads import gen_workload
+    from workloads import alibi_slopes, gen_workload
     q, k, v = gen_workload(w, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    slopes = torch.tensor(alibi_slopes(w.Hq), dtype=torch.float32, device="cuda") if alibi else None
 
     def step():
-        rf.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, rope_base=w.rope_base, out=o, lse=lse)
+        rf.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, rope_base=w.rope_base, out=o, lse=lse,
+               alibi_slopes=slopes)
 
-    ms = time_loop(step, steps, warmup)
+    t = time_steps(step, steps, warmup)
+    ms = t["mean"]
     flops = alg_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -138,13 +150,14 @@ def run_prefill(w, steps, warmup):
     gbs = byts / (ms * 1e-3) / 1e9
     traffic = traffic_from_profiles("fwd", w.name)
     res = {
-        "workload": w.name, "ms": ms, "TFLOP/s": tflops, "GB/s": gbs,
+        "workload": w.name, "ms": ms, "ms_median": t["median"], "ms_min": t["min"],
+        "TFLOP/s": tflops, "GB/s": gbs,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": tflops / peak, "traffic": traffic},
         "hbm_frac": gbs / PEAK_HBM_GBS,
         "alg_gflop": flops / 1e9, "alg_mb": byts / 1e6,
     }
-    return res, (q, k, v)
+    return res, (q, k, v, o, lse)
 
 
 def run_backward(w, steps, warmup):
@@ -218,12 +231,15 @@ def run_topk(steps, warmup):
             "alg_mb": byts / 1e6}
 
 
-def run_decode(w, steps, warmup):
+def run_decode(w, steps, warmup, num_splits=None, keep=False):
+    """Split-KV partials + merge on a decode workload.  num_splits defaults to
+    the workload's own (the decode config fixes 64 chunks of 512); the
+    decode geometries take the library's rule (rf_splitkv_num_splits)."""
     import torch
     import attention_pass_cascaded_amd as rf
     from workloads import gen_workload
     q, k, v = gen_workload(w, device="cuda")
-    S = w.num_splits
+    S = int(num_splits or w.num_splits or rf.num_splits_for(q, k))
     op = torch.empty((w.B, w.Hq, w.Nq, S, w.D), dtype=torch.float32, device="cuda")
     lp = torch.empty((w.B, w.Hq, w.Nq, S), dtype=torch.float32, device="cuda")
     o = torch.empty_like(q)
@@ -240,50 +256,170 @@ def run_decode(w, steps, warmup):
         part()
         merge()
 
-    ms = time_loop(step, steps, warmup)
+    t = time_steps(step, steps, warmup)
+    ms = t["mean"]
     ms_part = time_loop(part, steps, warmup)
     ms_merge = time_loop(merge, steps, warmup)
     byts = alg_bytes(w)
     gbs = byts / (ms * 1e-3) / 1e9
     gbs_part = byts / (ms_part * 1e-3) / 1e9
     traffic = traffic_from_profiles("decode", w.name)
-    return {
-        "workload": w.name, "value": gbs, "unit": "GB/s", "ms_per_step": ms,
+    res = {
+        "workload": w.name, "num_splits": S, "value": gbs, "unit": "GB/s", "ms_per_step": ms,
+        "ms_median": t["median"], "ms_min": t["min"],
         "ms_partial_kernel": ms_part, "ms_merge_kernel": ms_merge,
         "roofline": {"bound": "hbm", "achieved": gbs_part, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs_part / PEAK_HBM_GBS, "traffic": traffic},
         "step_frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
         "alg_mb": byts / 1e6, "alg_gflop": alg_flops(w) / 1e9,
     }
+    if keep:
+        return res, (q, k, v, o, lse)
+    return res
 
 
-def cpu_baseline(w, q, k, v, heads: int):
-    """The fp64 oracle on the workload (or batch 0's first `heads` heads)."""
-    import oracle
+def decode_geometries(steps, warmup, sweep=False):
+    """AttnFuse Table 8's three decode geometries at batch 1 and 16 (bf16,
+    Q.N = 1), each with num_splits from the library's rule; with ``sweep``
+    also every power of two from 8 to 256 chunks."""
+    from workloads import TABLE8_DECODE
+    out = []
+    for w in TABLE8_DECODE:
+        r = run_decode(w, steps, warmup)
+        row = {"workload": w.name, "num_splits": r["num_splits"], "ms_per_step": r["ms_per_step"],
+               "ms_median": r["ms_median"], "GB/s": r["value"], "step_frac_of_hbm_peak": r["step_frac_of_hbm_peak"],
+               "partial_GB/s": r["roofline"]["achieved"], "partial_frac": r["roofline"]["frac"]}
+        if sweep:
+            row["sweep_ms"] = {}
+            for S in (8, 16, 32, 64, 128, 256):
+                if S <= w.Nk:
+                    row["sweep_ms"][S] = run_decode(w, steps, warmup, num_splits=S)["ms_per_step"]
+        print(f"# decode {w.name}: S={row['num_splits']} {row['ms_per_step']:.4f} ms {row['GB/s']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        out.append(row)
+    return out
+
+
+VARIANT_SET = [  # AttnFuse Tables 6-7's variants, at the causal headline's shape
+    ("dense", dict(mask="none")),
+    ("causal", dict(mask="causal")),
+    ("sliding_w256", dict(mask="sliding", window=256)),
+    ("causal_alibi", dict(mask="causal", alibi=True)),
+    ("dense_rope", dict(mask="none", rope_base=10000.0)),
+    ("sliding_w256_rope", dict(mask="sliding", window=256, rope_base=10000.0)),
+]
+
+
+def variants_table(steps, warmup):
+    """Time each variant at B=4 H=12 N=4096 D=64 fp16 (absolute time and
+    roofline fraction; flops over the variant's own visible pairs)."""
+    import dataclasses
+    from workloads import by_name
+    base = by_name(HEADLINE)
+    rows = {}
+    for name, kw in VARIANT_SET:
+        kw = dict(kw)
+        alibi = kw.pop("alibi", False)
+        w = dataclasses.replace(base, name=f"{name}_f16_b4h12_n4096_d64", mask=kw.get("mask", "none"),
+                                window=kw.get("window", 0), rope_base=kw.get("rope_base", 0.0))
+        r, _ = run_prefill(w, steps, warmup, alibi=alibi)
+        rows[name] = {"ms": r["ms"], "ms_median": r["ms_median"], "TFLOP/s": r["TFLOP/s"],
+                      "mfma_frac": r["roofline"]["frac"], "GB/s": r["GB/s"], "hbm_frac": r["hbm_frac"],
+                      "alg_gflop": r["alg_gflop"]}
+        print(f"# variant {name}: {r['ms']:.4f} ms {r['TFLOP/s']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    return rows
+
+
+def host_cores() -> tuple[int, dict]:
+    """Threads for the oracle: the cores this process may run on
+    (sched_getaffinity), capped by the cgroup CPU quota when one is set."""
+    aff = len(os.sched_getaffinity(0))
+    quota = None
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    if heads <= 0:
-        qs, ks, vs = q.cpu(), k.cpu(), v.cpu()
-        heads = w.B * w.Hq
-    else:
-        qs = q[:1, :heads].cpu()
-        ks = k[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
-        vs = v[:1, : max(1, heads * w.Hkv // w.Hq)].cpu()
-    t0 = time.perf_counter()
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=cores):
-            oracle.attention(qs, ks, vs, w.scale, w.mask, w.window, w.rope_base)
-    else:
-        oracle.attention(qs, ks, vs, w.scale, w.mask, w.window, w.rope_base)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.D * visible_pairs(w.Nq, w.Nk, w.mask, w.window) * heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"whole {w.name} workload" if heads == w.B * w.Hq else
-                       f"batch 0, heads 0..{heads - 1} of {w.name} ({heads}/{w.B * w.Hq} of the workload)")
-                      + f", {flops / 1e9:.2f} GFLOP in {dt:.1f} s, float64 numpy three-pass oracle"}
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = max(1, math.ceil(int(q) / int(per)))
+    except (OSError, ValueError):
+        pass
+    return (min(aff, quota) if quota else aff), {"affinity_cores": aff, "cgroup_quota_cores": quota}
+
+
+def blas_backend() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{d.get('internal_api')} {d.get('version')} ({d.get('threading_layer')}, {d.get('architecture')})"
+                for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            return "; ".join(libs)
+    except Exception:  # pragma: no cover
+        pass
+    import numpy
+    return str(numpy.__config__.CONFIG.get("Build Dependencies", {}).get("blas", {}).get("name"))
+
+
+def oracle_leg(runs):
+    """The fp64 oracle beside each config (every element of every config),
+    on the host cores: its wall time (slice copies excluded) and the kernel's
+    whole-output error against it.  ``runs``: list of (workload, (q, k, v, o, lse))."""
+    from oracle import report
+    from threadpoolctl import threadpool_limits
+    cores, core_info = host_cores()
+    per_config, parity = [], []
+    with threadpool_limits(limits=cores):
+        for w, (q, k, v, o, lse) in runs:
+            t0 = time.perf_counter()
+            rep = report.compare_full(q, k, v, o, lse, w.scale, w.mask, w.window, w.rope_base, q.dtype)
+            wall = time.perf_counter() - t0
+            flops = alg_flops(w)
+            tol = {"f32": 2e-3, "f16": 2e-3, "bf16": 1e-2}[w.dtype]
+            per_config.append({"workload": w.name, "oracle_s": rep["oracle_s"], "wall_s_with_compare": wall,
+                               "TFLOP/s": flops / rep["oracle_s"] / 1e12, "sample": "whole workload"})
+            parity.append({"workload": w.name, "tol": tol, "max_abs_o": rep["max_abs_o"],
+                           "max_abs_lse": rep["max_abs_lse"], "floor": rep["floor"], "ulps": rep["ulps"],
+                           "worst": rep["worst"],
+                           "pass": rep["max_abs_o"] <= tol and rep["max_abs_lse"] <= tol})
+            print(f"# oracle {w.name}: {rep['oracle_s']:.1f} s; max|dO| {rep['max_abs_o']:.2e} "
+                  f"(floor {rep['floor']:.2e}, {rep['ulps']:.0f} ulp) max|dLSE| {rep['max_abs_lse']:.2e}",
+                  file=sys.stderr, flush=True)
+    return cores, core_info, per_config, parity
+
+
+def sample_clock(fn, seconds: float = 1.5):
+    """Shader clock while ``fn`` runs back to back: rocm-smi (or amd-smi) is
+    started as a child process while another thread keeps the GPU busy.
+    Returns the MHz values it printed for the graphics clock, or the reason
+    none was read."""
+    import subprocess
+    import threading
+    import torch
+    stop = threading.Event()
+
+    def load():
+        while not stop.is_set():
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+
+    th = threading.Thread(target=load, daemon=True)
+    th.start()
+    time.sleep(min(0.5, seconds / 3))
+    found, raw = [], ""
+    try:
+        for cmd in (["rocm-smi", "--showclocks", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
+            try:
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+            except (OSError, subprocess.TimeoutExpired) as e:
+                raw += f"{cmd[0]}: {e}; "
+                continue
+            raw += r.stdout[-400:]
+            for key, val in re.findall(r'"([^"]*(?:sclk|gfx|GFX)[^"]*)"\s*:\s*"?([^",}]*)', r.stdout):
+                found += [int(x) for x in re.findall(r"(\d{3,4})\s*[Mm][Hh]z", val)]
+            if found:
+                return {"tool": cmd[0], "MHz": sorted(set(found))}
+    finally:
+        stop.set()
+        th.join()
+    return {"tool": None, "MHz": None, "raw": raw[-600:]}
 
 
 def rotation_sweep(steps: int, warmup: int, Ns=(512, 1024, 2048, 4096, 8192, 16384)):
@@ -364,8 +500,10 @@ def main():
     ap.add_argument("--only-bwd", default=None, metavar="WORKLOAD", help="time the backward of one prefill workload")
     ap.add_argument("--only-layernorm", action="store_true", help="time the LayerNorm workload only")
     ap.add_argument("--only-topk", action="store_true", help="time the softmax-TopK workload only")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="heads of batch 0 for the oracle (0: whole workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (timing and parity)")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="decode geometries with every chunk count 8..256 (prints one JSON line)")
+    ap.add_argument("--variants", action="store_true", help="the variant table only (prints one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--rotation-sweep", action="store_true",
                     help="fused RoPE vs rotate-first over N (prints one JSON line per N)")
@@ -378,7 +516,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from workloads import by_name
+    from workloads import WORKLOADS, by_name
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -389,7 +527,12 @@ def main():
     if args.rotation_sweep:
         rotation_sweep(args.steps, args.warmup)
         return
-
+    if args.decode_sweep:
+        print(json.dumps({"decode_geometries": decode_geometries(args.steps, args.warmup, sweep=True)}), flush=True)
+        return
+    if args.variants:
+        print(json.dumps({"variants_table": variants_table(args.steps, args.warmup)}), flush=True)
+        return
     if args.only_topk:
         print(json.dumps(run_topk(args.steps, args.warmup)), flush=True)
         return
@@ -401,21 +544,44 @@ def main():
         return
     if args.only:
         w = by_name(args.only)
-        res = run_decode(w, args.steps, args.warmup) if w.num_splits else run_prefill(w, args.steps, args.warmup)[0]
+        res = (run_decode(w, args.steps, args.warmup) if w.num_splits or w.Nq == 1
+               else run_prefill(w, args.steps, args.warmup)[0])
         print(json.dumps(res), flush=True)
         return
 
+    # the headline: one step = one fused forward over the causal fp16 workload
     w = by_name(HEADLINE)
-    head, (q, k, v) = run_prefill(w, args.steps, args.warmup)
-    print(f"# headline {w.name}: {head['ms']:.4f} ms, {head['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    dec = run_decode(by_name(DECODE), args.steps, args.warmup)
-    print(f"# decode: {dec['ms_per_step']:.4f} ms, {dec['value']:.0f} GB/s", file=sys.stderr, flush=True)
-    variants = {}
-    for name in VARIANTS:
-        r, _ = run_prefill(by_name(name), args.steps, args.warmup)
-        variants[name] = {"ms": r["ms"], "TFLOP/s": r["TFLOP/s"], "GB/s": r["GB/s"],
-                          "mfma_frac": r["roofline"]["frac"], "hbm_frac": r["hbm_frac"]}
-        print(f"# {name}: {r['ms']:.4f} ms", file=sys.stderr, flush=True)
+    head, head_t = run_prefill(w, args.steps, args.warmup)
+    print(f"# headline {w.name}: {head['ms']:.4f} ms (median {head['ms_median']:.4f}, min {head['ms_min']:.4f}), "
+          f"{head['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    import attention_pass_cascaded_amd as rf
+    q, k, v, o, lse = head_t
+    clock = sample_clock(lambda: rf.fwd(q, k, v, scale=w.scale, mask=w.mask, out=o, lse=lse))
+    print(f"# shader clock under the headline's load: {clock}", file=sys.stderr, flush=True)
+
+    # every config in the same run: timing, then the oracle beside it
+    configs, runs = {}, []
+    for cw in WORKLOADS:
+        if cw.name == HEADLINE:
+            r, t = head, head_t
+        elif cw.num_splits:
+            r, t = run_decode(cw, args.steps, args.warmup, keep=True)
+        else:
+            r, t = run_prefill(cw, args.steps, args.warmup)
+        runs.append((cw, t))
+        if cw.num_splits:
+            configs[cw.name] = {"ms": r["ms_per_step"], "ms_median": r["ms_median"], "ms_min": r["ms_min"],
+                                "GB/s": r["value"], "num_splits": r["num_splits"],
+                                "ms_partial_kernel": r["ms_partial_kernel"], "ms_merge_kernel": r["ms_merge_kernel"],
+                                "roofline": r["roofline"], "step_frac_of_hbm_peak": r["step_frac_of_hbm_peak"]}
+        else:
+            configs[cw.name] = {"ms": r["ms"], "ms_median": r["ms_median"], "ms_min": r["ms_min"],
+                                "TFLOP/s": r["TFLOP/s"], "GB/s": r["GB/s"], "roofline": r["roofline"],
+                                "hbm_frac": r["hbm_frac"]}
+        print(f"# {cw.name}: {configs[cw.name]['ms']:.4f} ms", file=sys.stderr, flush=True)
+    dec = configs[DECODE]
+    geo = decode_geometries(args.steps, args.warmup)
+    var = variants_table(args.steps, args.warmup)
     bwd = run_backward(w, max(1, args.steps // 4), max(1, args.warmup // 4))
     print(f"# backward {w.name}: {bwd['ms']:.4f} ms, {bwd['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     ln = run_layernorm(args.steps, args.warmup)
@@ -424,7 +590,20 @@ def main():
     print(f"# softmax-topk {tk['workload']}: {tk['ms']:.4f} ms, {tk['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
     copy_gbs = copy_rate()
     print(f"# device copy: {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, q, k, v, args.cpu_heads)
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        cores, core_info, per_config, parity = oracle_leg(runs)
+        for pc in per_config:
+            configs[pc["workload"]]["oracle_s"] = pc["oracle_s"]
+        for pr in parity:
+            configs[pr["workload"]]["max_abs_o"] = pr["max_abs_o"]
+            configs[pr["workload"]]["max_abs_lse"] = pr["max_abs_lse"]
+        hp = next(pc for pc in per_config if pc["workload"] == HEADLINE)
+        cpu = {"value": hp["TFLOP/s"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"whole {HEADLINE} workload ({alg_flops(w) / 1e9:.2f} GFLOP) in {hp['oracle_s']:.1f} s, "
+                         "float64 numpy three-pass oracle, one (batch, KV head) group at a time",
+               "blas": blas_backend(), **core_info, "per_config": per_config}
 
     # The pages' own time for this exact workload (AttnFuse's dispatched
     # kernel, Table 3 / Table 2 BN=64 winner: 0.488 ms on an H100 NVL),
@@ -434,6 +613,7 @@ def main():
     line = {
         "metric": METRIC, "value": head["TFLOP/s"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms"],
+        "ms_per_step_median": head["ms_median"], "ms_per_step_min": head["ms_min"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": head["TFLOP/s"] / pages_tflops,
         "baseline_ref": {"value": pages_tflops, "unit": "TFLOP/s", "ms": PAGES_HEADLINE_MS,
                          "hardware": "H100 NVL", "source": "AttnFuse Table 3 (dispatched kernel)"},
@@ -443,8 +623,12 @@ def main():
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "none (1 GPU)"},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "shader_clock": clock,
+        "configs": configs,
+        "parity": parity,
         "decode": dec,
-        "variants": variants,
+        "decode_geometries": geo,
+        "variants_table": var,
         "backward": bwd,
         "layernorm": ln,
         "softmax_topk": tk,

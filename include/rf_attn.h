@@ -123,6 +123,22 @@ rf_status rf_attn_splitkv_fwd_alibi(const void* q, const void* k, const void* v,
                                     hipStream_t stream);
 
 /*
+ * rf_splitkv_num_splits — a chunk count for rf_attn_splitkv_fwd (the split
+ * of FlashDecoding, RedFuser Fig. 13; the decode geometries of AttnFuse
+ * Table 8).  The pages fix no rule; this one is measured on MI355X.  The
+ * partial kernel runs one work-group per (chunk, KV head, batch), so
+ *   S = ceil(RF_SPLIT_GROUPS_PER_CU * cu_count / (B * Hkv)),
+ * enough work-groups to keep every compute unit streaming, then capped so
+ * every chunk keeps at least RF_SPLIT_MIN_KEYS keys (S <= ceil(Nk /
+ * RF_SPLIT_MIN_KEYS)), and clamped to [1, 4096].  cu_count <= 0 asks the
+ * current device (falls back to 256).  Returns 0 for invalid sizes (B < 1,
+ * Hkv < 1, Nk < 0).
+ */
+#define RF_SPLIT_GROUPS_PER_CU 4
+#define RF_SPLIT_MIN_KEYS 256
+int rf_splitkv_num_splits(int B, int Hkv, int Nk, int cu_count);
+
+/*
  * rf_splitkv_workspace_bytes — bytes of o_part plus lse_part for the given
  * sizes: B*Hq*Nq*num_splits*(D + 1)*4.  Returns 0 for invalid sizes.
  */

@@ -26,7 +26,7 @@ import math
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "gen_qkv", "gen_normal", "alibi_slopes", "gen_grad_out",
+__all__ = ["Workload", "WORKLOADS", "TABLE8_DECODE", "by_name", "gen_qkv", "gen_normal", "alibi_slopes", "gen_grad_out",
            "LN_WORKLOAD", "gen_layernorm", "TOPK_WORKLOAD", "gen_logits"]
 
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -74,8 +74,20 @@ WORKLOADS = [
 ]
 
 
+# AttnFuse Table 8's flash-decoding geometries (query length 1; the table
+# states neither batch nor dtype): 32q/8kv/128 with 4096 and 16384 cached
+# keys and 64q/8kv/128 with 32768, each at batch 1 and 16, bf16 like the
+# decode workload above.  num_splits = 0: the library's chunk-count rule.
+TABLE8_DECODE = [
+    Workload(f"decode_bf16_b{B}_{Hq}q8kv_nk{Nk}_d128", B=B, Hq=Hq, Hkv=8, Nq=1, Nk=Nk, D=128, dtype="bf16",
+             scale=1.0 / math.sqrt(128), mask="none", num_splits=0, seed=seed)
+    for seed, (B, Hq, Nk) in enumerate([(1, 32, 4096), (16, 32, 4096), (1, 64, 32768), (16, 64, 32768),
+                                        (1, 32, 16384), (16, 32, 16384)], start=11)
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS:
+    for w in WORKLOADS + TABLE8_DECODE:
         if w.name == name:
             return w
     raise KeyError(name)
