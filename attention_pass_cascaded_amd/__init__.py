@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     RFError,
     bwd,
+    bwd_noalloc,
     decode,
     fwd,
     fwd_prerotated,
@@ -23,5 +24,5 @@ from ._binding import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["fwd", "bwd", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "softmax_topk", "workspace_bytes", "num_splits_for", "load_library",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "splitkv_fwd", "lse_merge", "decode", "rope_rotate", "fwd_prerotated", "layernorm", "softmax_topk", "workspace_bytes", "num_splits_for", "load_library",
            "RFError", "LIB_PATH", "EXPORTED"]

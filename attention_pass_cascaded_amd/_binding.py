@@ -25,7 +25,7 @@ _MASK = {"none": 0, "causal": 1, "sliding": 2}
 
 EXPORTED = ("rf_attn_fwd", "rf_attn_splitkv_fwd", "rf_attn_fwd_alibi", "rf_attn_splitkv_fwd_alibi",
             "rf_splitkv_num_splits", "rf_splitkv_workspace_bytes", "rf_lse_merge", "rf_rope_rotate", "rf_attn_bwd",
-            "rf_attn_bwd_workspace_bytes", "rf_layernorm_fwd", "rf_softmax_topk", "rf_status_string",
+            "rf_attn_bwd_workspace_bytes", "rf_attn_bwd_noalloc", "rf_layernorm_fwd", "rf_softmax_topk", "rf_status_string",
             "rf_last_error")
 
 
@@ -66,6 +66,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rf_rope_rotate.restype = i
     lib.rf_attn_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, i, f, i, i, f, vp, i, vp]
     lib.rf_attn_bwd.restype = i
+    lib.rf_attn_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, f, vp, i, vp]
+    lib.rf_attn_bwd_noalloc.restype = i
     lib.rf_attn_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.rf_attn_bwd_workspace_bytes.restype = sz
     lib.rf_layernorm_fwd.argtypes = [vp] * 6 + [i, i, f, i, vp]
@@ -284,6 +286,32 @@ def bwd(q, k, v, o, lse, dout, scale=None, mask="none", window=0, rope_base=0.0,
     _check(lib.rf_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                            _ptr(dv), _ptr(workspace), B, Hq, Hkv, Nq, Nk, D, _scale(scale, D), _MASK[mask],
                            int(window), float(rope_base), _ptr(slopes), _DTYPE[q.dtype], _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale=None, mask="none", window=0, rope_base=0.0,
+                alibi_slopes=None):
+    """rf_attn_bwd_noalloc: the gradients into the caller's dq, dk, dv with
+    the row terms in the library's static per-GPU array (no workspace; calls
+    that overlap on one GPU race).  alibi_slopes must then be a float32 [Hq]
+    GPU tensor (a sequence would be copied to a new device tensor)."""
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
+        if not t.is_cuda or t.dtype != q.dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            raise ValueError(f"{name} must be provided")
+        _out(name, t, like.shape, like.dtype, q.device)
+    if alibi_slopes is not None and not (isinstance(alibi_slopes, torch.Tensor) and alibi_slopes.is_cuda):
+        raise ValueError("alibi_slopes must be a float32 [Hq] GPU tensor here")
+    slopes = _slopes(alibi_slopes, Hq, q.device)
+    _check(load_library().rf_attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq,
+        Nk, D, _scale(scale, D), _MASK[mask], int(window), float(rope_base), _ptr(slopes), _DTYPE[q.dtype],
+        _stream(q)))
     return dq, dk, dv
 
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "bwd_kernel.hpp"
@@ -246,10 +247,46 @@ size_t rf_attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
     return (size_t)B * Hq * Nq * sizeof(float);
 }
 
-rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dout, void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv,
-                      int Nq, int Nk, int D, float scale, int mask_kind, int window, float rope_base,
-                      const float* alibi_slopes, int dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Row terms of rf_attn_bwd_noalloc: one library-owned array per GPU, kept
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it only names the symbol); it uses the device address
+// hipGetSymbolAddress returns, fetched once per device with that device
+// current and cached here.
+static __device__ __align__(256) float scratch[RF_BWD_NOALLOC_MAX_ROWS];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];
+
+rf_status scratch_for_current_device(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(RF_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(RF_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+        g_scratch_ptr[dev] = (float*)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return RF_OK;
+}
+
+// Validation and launch shared by rf_attn_bwd and rf_attn_bwd_noalloc.
+// workspace == nullptr with use_scratch: the row terms go to this device's
+// scratch array (B*Hq*Nq <= RF_BWD_NOALLOC_MAX_ROWS, checked before the
+// array's address is fetched).
+rf_status attn_bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* workspace, bool use_scratch,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale, int mask_kind, int window,
+                        float rope_base, const float* alibi_slopes, int dtype, hipStream_t stream) {
     rf::AttnParams a;
     rf_status st = check_attn(q, k, v, B, Hq, Hkv, Nq, Nk, D, scale, mask_kind, window, rope_base, dtype, a);
     if (st != RF_OK) return st;
@@ -257,7 +294,10 @@ rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o
     if (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) return fail(RF_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     const bool q_nonempty = (size_t)B * Nq > 0;
     const bool kv_nonempty = (size_t)B * Nk > 0;
-    if (q_nonempty && (!o || !lse || !dout || !dq || !workspace))
+    if (use_scratch && (size_t)B * Hq * Nq > (size_t)RF_BWD_NOALLOC_MAX_ROWS)
+        return fail(RF_ERR_UNSUPPORTED, "B*Hq*Nq = %zu rows exceed the %d rows of the static row-term array",
+                    (size_t)B * Hq * Nq, RF_BWD_NOALLOC_MAX_ROWS);
+    if (q_nonempty && (!o || !lse || !dout || !dq || (!workspace && !use_scratch)))
         return fail(RF_ERR_INVALID_ARG, "o, lse, dout, dq and workspace are required");
     if (kv_nonempty && (!dk || !dv)) return fail(RF_ERR_INVALID_ARG, "dk and dv are required");
     if ((o && !aligned16(o)) || (dout && !aligned16(dout)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
@@ -267,6 +307,10 @@ rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o
         (size_t)B * Hkv * ((Nk + rf::BWD_BK - 1) / rf::BWD_BK) > 0x7fffffffu)
         return fail(RF_ERR_INVALID_ARG, "grid too large");
     if (!q_nonempty && !kv_nonempty) return RF_OK;
+    if (use_scratch) {
+        st = scratch_for_current_device(&workspace);
+        if (st != RF_OK) return st;
+    }
     rf::BwdParams p{};
     p.q = q;
     p.k = k;
@@ -292,6 +336,26 @@ rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o
     p.rope = a.rope;
     const hipError_t e = dtype == RF_F16 ? rf::launch_bwd_f16(p, stream) : rf::launch_bwd_bf16(p, stream);
     return hip_status(e, "rf_attn_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int D, float scale, int mask_kind, int window, float rope_base,
+                      const float* alibi_slopes, int dtype, hipStream_t stream) {
+    return attn_bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, false, B, Hq, Hkv, Nq, Nk, D, scale,
+                         mask_kind, window, rope_base, alibi_slopes, dtype, stream);
+}
+
+rf_status rf_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                              int Nk, int D, float scale, int mask_kind, int window, float rope_base,
+                              const float* alibi_slopes, int dtype, hipStream_t stream) {
+    return attn_bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, true, B, Hq, Hkv, Nq, Nk, D, scale,
+                         mask_kind, window, rope_base, alibi_slopes, dtype, stream);
 }
 
 rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,

@@ -204,6 +204,28 @@ rf_status rf_attn_bwd(const void* q, const void* k, const void* v, const void* o
 size_t rf_attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 
 /*
+ * rf_attn_bwd_noalloc — rf_attn_bwd without the workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The row terms D_i
+ * go to a static device array owned by the library, RF_BWD_NOALLOC_MAX_ROWS
+ * floats (16 MiB) on each GPU the library runs on, held until the process
+ * ends; its address is looked up once per device on the first call made
+ * with that device current.  Nothing is allocated and no memset is issued
+ * (the array needs no clearing: every row term is written before it is
+ * read).  B*Hq*Nq above RF_BWD_NOALLOC_MAX_ROWS returns RF_ERR_UNSUPPORTED
+ * before anything is launched.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  Other arguments, results and errors
+ * as rf_attn_bwd.
+ */
+#define RF_BWD_NOALLOC_MAX_ROWS (1 << 22)
+rf_status rf_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                              float scale, int mask_kind, int window, float rope_base,
+                              const float* alibi_slopes, int dtype, hipStream_t stream);
+
+/*
  * rf_layernorm_fwd — LayerNorm, a second cascaded reduction run through the
  * same incremental machinery (RedFuser abstract and Table 1: a later
  * reduction that reads an earlier one's result; "Operator Fusion" guide,

@@ -225,3 +225,24 @@ def test_out_buffer_on_another_device_rejected():
 ])
 def test_num_splits_rule(lib, B, Hkv, Nk, cu, want):
     assert lib.rf_splitkv_num_splits(B, Hkv, Nk, cu) == want
+
+
+def bwd_noalloc(lib, **kw):
+    a = dict(B=1, Hq=2, Hkv=2, Nq=8, Nk=8, D=64, scale=0.125, mask=1, window=0, rope=0.0, dtype=1)
+    a.update(kw)
+    return lib.rf_attn_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"],
+                                   a["Nq"], a["Nk"], a["D"], a["scale"], a["mask"], a["window"], a["rope"], None,
+                                   a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    # one row past the static row-term array (2^22 rows): refused before any launch
+    (dict(B=1, Hq=64, Hkv=64, Nq=(1 << 16) + 1, Nk=8), B.RF_ERR_UNSUPPORTED, "static row-term array"),
+    (dict(B=2, Hq=32, Hkv=8, Nq=65537, Nk=8), B.RF_ERR_UNSUPPORTED, "static row-term array"),
+    (dict(dtype=0), B.RF_ERR_UNSUPPORTED, "float16 and bfloat16"),
+    (dict(Hq=3, Hkv=2), B.RF_ERR_INVALID_ARG, "multiple"),
+    (dict(D=96), B.RF_ERR_UNSUPPORTED, "96"),
+])
+def test_bwd_noalloc_rejects_before_launch(lib, kw, status, needle):
+    assert bwd_noalloc(lib, **kw) == status
+    assert needle in lib.rf_last_error().decode()
