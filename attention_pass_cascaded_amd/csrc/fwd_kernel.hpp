@@ -58,6 +58,43 @@ struct FwdCfg {
 #define RF_FWD_WAVES_D64 4
 #endif
 
+// Work-group order (one-dimensional grid of B*Hq*S*nqb query blocks of
+// FWD_BM rows); returns the query block qb and bx = (b * Hq + h) * S + split.
+//  causal: every head's heaviest (latest) query blocks first, then lighter
+//    ones, so the uneven blocks balance across the CUs.  The groups that
+//    start at launch are placed statically: group pid goes to the CU
+//    numbered pid mod P (P CUs), so a CU receives items pid, pid + P,
+//    pid + 2P, ...  When the whole grid is resident at launch, every other
+//    run of P items is taken in reverse (snake order), which gives each CU
+//    a heavy item from one run and a light one from the next instead of
+//    items of the same rank.  A larger grid keeps the plain order: its
+//    later groups start wherever a slot frees, which balances by itself;
+//  no mask / sliding window (every block costs the same): the dispatcher
+//    deals work-groups round-robin over the XCDs (each with its own L2), so
+//    renumber to give every XCD a contiguous run of one head's query blocks
+//    and keep the K/V tiles that neighbouring blocks share in its L2.
+__device__ __forceinline__ void fwd_work_item(const AttnParams& p, int nqb, int& qb, int& bx) {
+    const int G = gridDim.x;
+    const int pid = blockIdx.x;
+    if (p.mask == RF_MASK_CAUSAL) {
+        const int heads = G / nqb;
+        const int P = p.cu_count;
+        int item = pid;  // index in heaviest-first order
+        if (P > 0 && (long long)P * p.launch_runs >= G) {
+            const int run = pid / P;
+            if ((run & 1) && run < G / P) item = run * P + (P - 1 - pid % P);
+        }
+        qb = nqb - 1 - item / heads;
+        bx = item % heads;
+    } else {
+        const int xcd = pid % NUM_XCD, local = pid / NUM_XCD;
+        const int per = G / NUM_XCD, rem = G % NUM_XCD;
+        const int L = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+        qb = L % nqb;
+        bx = L / nqb;
+    }
+}
+
 template <typename T, int D, bool ROPE, bool ALIBI>
 __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
@@ -89,41 +126,9 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    // Work-group order (one-dimensional grid of B*Hq*S*nqb).
-    //  causal: every head's heaviest (latest) query blocks first, then lighter
-    //    ones, so the uneven blocks balance across the CUs.  The groups that
-    //    start at launch are placed statically: group pid goes to the CU
-    //    numbered pid mod P (P CUs), so a CU receives items pid, pid + P,
-    //    pid + 2P, ...  When the whole grid is resident at launch, every other
-    //    run of P items is taken in reverse (snake order), which gives each CU
-    //    a heavy item from one run and a light one from the next instead of
-    //    items of the same rank.  A larger grid keeps the plain order: its
-    //    later groups start wherever a slot frees, which balances by itself;
-    //  no mask / sliding window (every block costs the same): the dispatcher
-    //    deals work-groups round-robin over the XCDs (each with its own L2), so
-    //    renumber to give every XCD a contiguous run of one head's query blocks
-    //    and keep the K/V tiles that neighbouring blocks share in its L2.
     const int nqb = (p.Nq + FWD_BM - 1) / FWD_BM;
-    const int G = gridDim.x;
-    const int pid = blockIdx.x;
     int qb, bx;  // bx = (b * Hq + h) * S + split
-    if (p.mask == RF_MASK_CAUSAL) {
-        const int heads = G / nqb;
-        const int P = p.cu_count;
-        int item = pid;  // index in heaviest-first order
-        if (P > 0 && (long long)P * p.launch_runs >= G) {
-            const int run = pid / P;
-            if ((run & 1) && run < G / P) item = run * P + (P - 1 - pid % P);
-        }
-        qb = nqb - 1 - item / heads;
-        bx = item % heads;
-    } else {
-        const int xcd = pid % NUM_XCD, local = pid / NUM_XCD;
-        const int per = G / NUM_XCD, rem = G % NUM_XCD;
-        const int L = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-        qb = L % nqb;
-        bx = L / nqb;
-    }
+    fwd_work_item(p, nqb, qb, bx);
     const int split = bx % p.num_splits;
     bx /= p.num_splits;
     const int h = bx % p.Hq;
