@@ -17,7 +17,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "librfattn.so")
+# RF_ATTN_LIB names another build of the same library (the sanitized host build)
+LIB_PATH = os.environ.get("RF_ATTN_LIB") or os.path.join(_PKG, "librfattn.so")
 
 RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP = 0, 1, 2, 3
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}

@@ -432,7 +432,7 @@ rf_status rf_softmax_topk(const void* x, float* values, int* indices, int rows, 
     return hip_status(hipGetLastError(), "rf_softmax_topk launch");
 }
 
-const char* rf_status_string(rf_status s) {
+const char* rf_status_string(int s) {
     switch (s) {
         case RF_OK: return "ok";
         case RF_ERR_INVALID_ARG: return "invalid argument";

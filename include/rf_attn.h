@@ -266,8 +266,9 @@ rf_status rf_layernorm_fwd(const void* x, const void* gamma, const void* beta, v
 rf_status rf_softmax_topk(const void* x, float* values, int* indices, int rows, int E, int k,
                           int dtype, hipStream_t stream);
 
-/* rf_status_string — static text for a status code. */
-const char* rf_status_string(rf_status s);
+/* rf_status_string — static text for a status code; any int is accepted
+ * (codes outside rf_status give "unknown status"). */
+const char* rf_status_string(int s);
 
 /* rf_last_error — thread-local detail for the calling thread's last non-OK return. */
 const char* rf_last_error(void);
