@@ -38,16 +38,17 @@ namespace rf {
 // operands keep ~16 mantissa bits; S then takes three MFMAs (hi.hi, hi.lo,
 // lo.hi).  Used for bf16 with RoPE, where rounding the rotated q and k to a
 // single bf16 dominates the output error.
-template <typename T, int D, bool SPLITK = false>
+template <typename T, int D, bool SPLITK = false, bool KH = false>
 struct FwdCfg {
     static constexpr bool F32 = sizeof(T) == 4;
-    static constexpr int BN = F32 ? 32 : 64;            // keys per tile
+    static constexpr int BN = (F32 || KH) ? 32 : 64;    // keys per tile
+    static constexpr int GT = KH ? FWD_THREADS / 2 : FWD_THREADS;  // threads staging one tile stream
     static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
     static constexpr int CPR = D / EPC;                 // chunks per row
     static constexpr int KSTRIDE = D + EPC;             // row pitch (elements), +16 B
     static constexpr int K_ELEMS = BN * KSTRIDE * (SPLITK ? 2 : 1);  // hi tile, then lo tile
     static constexpr int STAGE = K_ELEMS + BN * KSTRIDE;  // + V tile, row-major
-    static constexpr int CH = BN * CPR / FWD_THREADS;   // 16-byte chunks per thread per tile
+    static constexpr int CH = BN * CPR / GT;            // 16-byte chunks per thread per tile
     static_assert(CH >= 2 && CH % 2 == 0, "tile must give each thread an even chunk count");
 };
 
@@ -95,10 +96,20 @@ __device__ __forceinline__ void fwd_work_item(const AttnParams& p, int nqb, int&
     }
 }
 
-template <typename T, int D, bool ROPE, bool ALIBI>
+// KH (key halves, 16-bit D = 64): 64 query rows per work-group, and the
+// work-group's key range is cut in two: waves 0-1 (group 0) take the first
+// half, waves 2-3 (group 1) the second, each with its own 32-key tile stream
+// and LDS double buffer; at the end group 1 hands (O, m, l) to group 0
+// through LDS and group 0 merges them (the LSE merge of two partial states,
+// RedFuser Fig. 13).  The longest chain of tile steps a work-group runs is
+// halved, which is what bounds a causal launch whose grid fits the GPU in
+// one wave of work-groups.
+template <typename T, int D, bool ROPE, bool ALIBI, bool KH = false>
 __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
-    using C = FwdCfg<T, D, SPLITK>;
+    using C = FwdCfg<T, D, SPLITK, KH>;
+    constexpr int GT = C::GT;
+    constexpr int BM = KH ? FWD_BM / 2 : FWD_BM;  // query rows per work-group
     constexpr bool F32 = C::F32;
     constexpr int BN = C::BN;
     constexpr int EPC = C::EPC;
@@ -117,28 +128,34 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     // lands under tile t's score products and softmax, and a second barrier
     // precedes the P.V.
     constexpr bool V1 = D == 128 && !F32 && !ROPE && !ALIBI;
+    static_assert(!KH || (D == 64 && !F32), "key halves: 16-bit D = 64");
 
-    __shared__ __attribute__((aligned(16))) T smem[V1 ? 2 * C::K_ELEMS + BN * KS : 2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) T smem[V1 ? 2 * C::K_ELEMS + BN * KS : (KH ? 4 : 2) * C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hi = lane >> 5;
+    // KH: group (key half) of this wave, its row slot, and the thread's index in the group
+    const int grp = KH ? wave >> 1 : 0;
+    const int rw = KH ? wave & 1 : wave;
+    const int gtid = KH ? tid & (GT - 1) : tid;
+    T* const gsm = KH ? smem + grp * 2 * C::STAGE : smem;  // this group's two stages
 
-    const int nqb = (p.Nq + FWD_BM - 1) / FWD_BM;
+    const int nqb = (p.Nq + BM - 1) / BM;
     int qb, bx;  // bx = (b * Hq + h) * S + split
     fwd_work_item(p, nqb, qb, bx);
     const int split = bx % p.num_splits;
     bx /= p.num_splits;
     const int h = bx % p.Hq;
     const int b = bx / p.Hq;
-    const int q0 = qb * FWD_BM;
+    const int q0 = qb * BM;
     const int g = h / (p.Hq / p.Hkv);
     const int pos_off = p.Nk - p.Nq;
 
     // Key range the whole work-group visits.
-    const int last_row = min(p.Nq, q0 + FWD_BM) - 1;
+    const int last_row = min(p.Nq, q0 + BM) - 1;
     int klo = split * p.split_len;
     int khi = min(p.Nk, klo + p.split_len);
     if (p.mask != RF_MASK_NONE) khi = min(khi, last_row + pos_off + 1);
@@ -152,12 +169,18 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     // any other.  (Other instances keep the plain ascending order and its code.)
     const bool cyc = V1 && p.mask == RF_MASK_SLIDING && !p.split_mode && khi > klo;
     if (cyc) klo -= klo % BN;
-    const int ntiles = khi > klo ? (khi - klo + BN - 1) / BN : 0;
+    const int ntiles_wg = khi > klo ? (khi - klo + BN - 1) / BN : 0;
+    // KH: group 0 takes tiles [0, n0), group 1 tiles [n0, ntiles_wg); both
+    // run n0 steps (group 1 idles in a last step it has no tile for).
+    const int n0 = KH ? (ntiles_wg + 1) / 2 : ntiles_wg;
+    const int ntiles = KH ? (grp ? ntiles_wg - n0 : n0) : ntiles_wg;  // this group's tiles
+    const int nsteps = n0;
+    const int kbeg = klo + (KH && grp ? n0 * BN : 0);                 // this group's first key
     // tile index at step 0, then +1 per step with wrap-around
     int tcur = cyc ? (ntiles - (klo / BN) % ntiles) % ntiles : 0;
 
     // This wave's rows and their positions.
-    const int wrow0 = q0 + 32 * wave;
+    const int wrow0 = q0 + 32 * rw;
     const bool wave_live = wrow0 < p.Nq;
     const int pw_min = wrow0 + pos_off;
     const int pw_max = min(p.Nq, wrow0 + 32) - 1 + pos_off;
@@ -227,13 +250,33 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         }
     }
 
-    // ---------------- RoPE constants for this thread's K chunks
-    // With RoPE the thread loads chunk cc and its partner cc + CPR/2 of a row.
-    double ipd[ROPE ? EPC : 1];
+    // ---------------- RoPE state for this thread's K chunks
+    // With RoPE the thread loads chunk cc and its partner cc + CPR/2 of rows
+    // row0 + j * RSTEP (j < CH/2) of each tile, so it rotates by the angles
+    // (k0 + row0 + j * RSTEP) * theta_d, d = cc * EPC + e.  Tiles are stored in
+    // key order, BN keys apart, so (rc, rs) = (cos, sin) of the j = 0 angle is
+    // carried from tile to tile by the angle-addition identity with the
+    // per-frequency step (cos, sin)(BN * theta_d), and rows j > 0 follow with
+    // (cos, sin)(RSTEP * theta_d); both steps sit in LDS.  Every
+    // ROPE_REANCHOR-th tile the angle is taken exactly again (fp64 fraction
+    // of revolutions, then v_sin/v_cos), so float rounding of the recurrence
+    // cannot build up over long key ranges.
+    constexpr int RSTEP = 2 * GT / CPR;  // rows between a thread's pairs
+    constexpr int ROPE_REANCHOR = 64;
+    float rc[ROPE ? EPC : 1], rs[ROPE ? EPC : 1];
+    __shared__ float2 rope_step[ROPE ? D : 1];     // [d]: BN * theta_d; [D/2 + d]: RSTEP * theta_d
+    __shared__ double rope_ip[ROPE ? D / 2 : 1];  // theta_d / (2 pi)
     if (ROPE) {
-        const int cc = tid % (CPR / 2);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) ipd[e] = p.rope.inv_period[cc * EPC + e];
+        if (tid < D / 2) {
+            const double ip = p.rope.inv_period[tid];
+            float c1, s1, c2, s2;
+            rope_cos_sin(ip, BN, c1, s1);
+            rope_cos_sin(ip, RSTEP, c2, s2);
+            rope_step[tid] = make_float2(c1, s1);
+            rope_step[D / 2 + tid] = make_float2(c2, s2);
+            rope_ip[tid] = ip;
+        }
+        __syncthreads();
     }
 
     // ---------------- tile staging
@@ -272,11 +315,11 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         for (int it = 0; it < C::CH; ++it) {
             int row, ch;
             if (ROPE) {  // pairs (cc, cc + CPR/2)
-                const int u = (it / 2) * FWD_THREADS + tid;
+                const int u = (it / 2) * GT + gtid;
                 row = u / (CPR / 2);
                 ch = u % (CPR / 2) + (it % 2) * (CPR / 2);
             } else {
-                const int u = it * FWD_THREADS + tid;
+                const int u = it * GT + gtid;
                 row = u / CPR;
                 ch = u % CPR;
             }
@@ -284,28 +327,54 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
-            const int u = it * FWD_THREADS + tid;
+            const int u = it * GT + gtid;
             vreg[it] = buf_load16(vrs, ((unsigned)(k0 + u / CPR) * D + (u % CPR) * EPC) * (unsigned)sizeof(T));
         }
     };
 
     auto store_tile = [&](int stage, int k0) {
-        T* ks_ = smem + stage * C::STAGE;
+        T* ks_ = gsm + stage * C::STAGE;
         T* vs_ = ks_ + C::K_ELEMS;
         if (ROPE) {
+            const int cc = gtid % (CPR / 2);
+            if (((k0 - kbeg) / BN) % ROPE_REANCHOR == 0) {
+                const int pos = k0 + gtid / (CPR / 2);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) rope_cos_sin(rope_ip[cc * EPC + e], pos, rc[e], rs[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    const float2 st = rope_step[cc * EPC + e];
+                    const float c_ = rc[e] * st.x - rs[e] * st.y;
+                    rs[e] = rs[e] * st.x + rc[e] * st.y;
+                    rc[e] = c_;
+                }
+            }
+            float cj[EPC], sj[EPC];  // angle of pair j, starting at row0
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                cj[e] = rc[e];
+                sj[e] = rs[e];
+            }
 #pragma unroll
             for (int it = 0; it < C::CH; it += 2) {
-                const int u = (it / 2) * FWD_THREADS + tid;
+                const int u = (it / 2) * GT + gtid;
                 const int row = u / (CPR / 2);
-                const int cc = u % (CPR / 2);
-                const int pos = k0 + row;
+                if (it > 0) {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) {
+                        const float2 st = rope_step[D / 2 + cc * EPC + e];
+                        const float c_ = cj[e] * st.x - sj[e] * st.y;
+                        sj[e] = sj[e] * st.x + cj[e] * st.y;
+                        cj[e] = c_;
+                    }
+                }
                 const VecT lo = *(const VecT*)&kreg[it];
                 const VecT hi_ = *(const VecT*)&kreg[it + 1];
                 VecT olo, ohi, rlo, rhi;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
-                    float cs, sn;
-                    rope_cos_sin(ipd[e], pos, cs, sn);
+                    const float cs = cj[e], sn = sj[e];
                     const float x = to_f32(lo[e]), y = to_f32(hi_[e]);
                     const float xr = x * cs - y * sn, yr = x * sn + y * cs;
                     olo[e] = from_f32<T>(xr);
@@ -326,13 +395,13 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         } else {
 #pragma unroll
             for (int it = 0; it < C::CH; ++it) {
-                const int u = it * FWD_THREADS + tid;
+                const int u = it * GT + gtid;
                 *(uint4*)(ks_ + (u / CPR) * KS + (u % CPR) * EPC) = kreg[it];
             }
         }
 #pragma unroll
         for (int it = 0; it < C::CH; ++it) {
-            const int u = it * FWD_THREADS + tid;
+            const int u = it * GT + gtid;
             *(uint4*)(vs_ + (u / CPR) * KS + (u % CPR) * EPC) = vreg[it];
         }
     };
@@ -356,19 +425,19 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         if constexpr (V1) {
             issue_rows(krs, smem, klo + tcur * BN);
         } else {
-            load_tile(klo);
-            store_tile(0, klo);
+            load_tile(kbeg);
+            store_tile(0, kbeg);
         }
     }
 
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = 0; t < nsteps; ++t) {
         int k0, k0n;  // this step's tile and the next one's
         if constexpr (V1) {
             k0 = klo + tcur * BN;
             tcur = tcur + 1 == ntiles ? 0 : tcur + 1;
             k0n = klo + tcur * BN;
         } else {
-            k0 = klo + t * BN;
+            k0 = kbeg + t * BN;
             k0n = k0 + BN;
         }
         const int stage = t & 1;
@@ -382,7 +451,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         }
 
         // wave-level skip / mask decisions
-        bool skip = !wave_live;
+        bool skip = !wave_live || t >= ntiles;
         bool need_mask = (k0 + BN > khi);
         if (p.mask != RF_MASK_NONE) {
             skip |= k0 > pw_max;
@@ -393,7 +462,7 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
             }
         }
 
-        const T* ks_ = V1 ? smem + stage * C::K_ELEMS : smem + stage * C::STAGE;
+        const T* ks_ = V1 ? smem + stage * C::K_ELEMS : gsm + stage * C::STAGE;
         const T* vs_ = V1 ? smem + 2 * C::K_ELEMS : ks_ + C::K_ELEMS;
         float pr[NKB][16];
         if (!skip) {
@@ -528,6 +597,36 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         if constexpr (!V1) {
             if (t + 1 < ntiles) store_tile(stage ^ 1, k0n);
         }
+    }
+
+    if constexpr (KH) {
+        // group 1 hands its state to group 0 through LDS, element-major
+        // ([value][row slot][lane]) so the 64 lanes hit 64 banks
+        constexpr int NV = NDB * 16 + 2;
+        float* xs = (float*)smem;
+        static_assert(2 * NV * 64 * sizeof(float) <= sizeof(smem), "merge area");
+        __syncthreads();  // every wave is done with the tile buffers
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) xs[((db * 16 + j) * 2 + rw) * 64 + lane] = oacc[db][j];
+            xs[((NV - 2) * 2 + rw) * 64 + lane] = m_ref;
+            xs[((NV - 1) * 2 + rw) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = xs[((NV - 2) * 2 + rw) * 64 + lane];
+        const float l1 = xs[((NV - 1) * 2 + rw) * 64 + lane];
+        const float mm = fmaxf(m_ref, m1);
+        const float a0 = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mm);  // -inf - -inf would be NaN
+        const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][j] = a0 * oacc[db][j] + a1 * xs[((db * 16 + j) * 2 + rw) * 64 + lane];
+        l_run = a0 * l_run + a1 * l1;
+        m_ref = mm;
     }
 
     // ---------------- epilogue: O /= l, lse = ln sum exp

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <atomic>
+#include <cstdlib>
 
 #include "bwd_kernel.hpp"
 #include "decode_kernel.hpp"
@@ -11,31 +12,63 @@
 
 namespace rf {
 
-template <typename T, int D, bool ROPE, bool ALIBI>
-hipError_t fwd_launch_one(const AttnParams& p, hipStream_t s) {
-    // work-groups of this instance that fit on one CU (cached; same for every gfx950 device)
+// work-groups of an instance that fit on one CU (cached per instance; the
+// same for every gfx950 device); 0 if the query fails
+template <typename T, int D, bool ROPE, bool ALIBI, bool KH>
+int fwd_resident() {
     static std::atomic<int> resident{0};
     int r = resident.load(std::memory_order_relaxed);
     if (r == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, attn_fwd_kernel<T, D, ROPE, ALIBI>, FWD_THREADS, 0) != hipSuccess) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, attn_fwd_kernel<T, D, ROPE, ALIBI, KH>, FWD_THREADS, 0) != hipSuccess) {
             r = 0;
             (void)hipGetLastError();  // a failed query only turns the snake order off
         }
         if (r > 0) resident.store(r, std::memory_order_relaxed);
         else r = 0;
     }
+    return r;
+}
+
+template <typename T, int D, bool ROPE, bool ALIBI, bool KH>
+hipError_t fwd_launch_one(const AttnParams& p, hipStream_t s) {
+    constexpr int BM = KH ? FWD_BM / 2 : FWD_BM;
     AttnParams q = p;
-    q.launch_runs = r;
-    dim3 grid((unsigned)(p.B * p.Hq * p.num_splits * ((p.Nq + FWD_BM - 1) / FWD_BM)));
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI>), grid, dim3(FWD_THREADS), 0, s, q);
+    q.launch_runs = fwd_resident<T, D, ROPE, ALIBI, KH>();
+    dim3 grid((unsigned)(p.B * p.Hq * p.num_splits * ((p.Nq + BM - 1) / BM)));
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI, KH>), grid, dim3(FWD_THREADS), 0, s, q);
     return hipGetLastError();
+}
+
+// Key halves (16-bit D = 64, not split mode) when twice the 128-row grid
+// still fits in the work-groups the GPU holds at once: then every work-group
+// starts at launch and halving the longest chain of tile steps shortens the
+// launch.  Measured slower once the doubled grid needs a second round (the
+// 32-key steps of the halves cost more per key).  The environment variable
+// RF_ATTN_KEY_HALVES=0 or =1 overrides the choice (read at every call).
+template <typename T, int D, bool ROPE, bool ALIBI>
+hipError_t fwd_launch_pick(const AttnParams& p, hipStream_t s) {
+    if constexpr (D == 64 && sizeof(T) == 2) {
+        if (!p.split_mode) {
+            const char* env = std::getenv("RF_ATTN_KEY_HALVES");
+            bool kh;
+            if (env && (env[0] == '0' || env[0] == '1') && env[1] == 0) {
+                kh = env[0] == '1';
+            } else {
+                const long long g = (long long)p.B * p.Hq * p.num_splits * ((p.Nq + FWD_BM - 1) / FWD_BM);
+                const long long slots = (long long)p.cu_count * fwd_resident<T, D, ROPE, ALIBI, true>();
+                kh = g > 0 && 2 * g <= slots;
+            }
+            if (kh) return fwd_launch_one<T, D, ROPE, ALIBI, true>(p, s);
+        }
+    }
+    return fwd_launch_one<T, D, ROPE, ALIBI, false>(p, s);
 }
 
 template <typename T, int D>
 hipError_t fwd_dispatch_d(const AttnParams& p, hipStream_t s) {
     const bool rope = p.rope_base > 0.f;
-    if (p.alibi) return rope ? fwd_launch_one<T, D, true, true>(p, s) : fwd_launch_one<T, D, false, true>(p, s);
-    return rope ? fwd_launch_one<T, D, true, false>(p, s) : fwd_launch_one<T, D, false, false>(p, s);
+    if (p.alibi) return rope ? fwd_launch_pick<T, D, true, true>(p, s) : fwd_launch_pick<T, D, false, true>(p, s);
+    return rope ? fwd_launch_pick<T, D, true, false>(p, s) : fwd_launch_pick<T, D, false, false>(p, s);
 }
 
 template <typename T>

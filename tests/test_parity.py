@@ -83,6 +83,11 @@ FWD_CASES = [
     ("bf16", 64, 1, 2, 1, 40, 1500, "none", 0, 10000.0),
     ("f16", 64, 1, 2, 2, 100, 1400, "sliding", 1200, 10000.0),
     ("f16", 64, 1, 1, 1, 16, 70000, "causal", 0, 10000.0),
+    # D = 128 RoPE: each thread rotates two rows of a K tile; long enough key
+    # ranges that the carried angle passes several exact re-anchors
+    ("f16", 128, 1, 2, 1, 130, 3000, "causal", 0, 10000.0),
+    ("bf16", 128, 1, 2, 2, 200, 5000, "sliding", 700, 500000.0),
+    ("f32", 128, 1, 1, 1, 50, 4500, "causal", 0, 10000.0),
     ("f32", 64, 1, 1, 1, 256, 256, "none", 0, 0.0),
     ("f32", 64, 1, 2, 2, 100, 100, "causal", 0, 10000.0),
     ("f32", 128, 1, 2, 1, 77, 150, "sliding", 40, 0.0),
@@ -98,6 +103,49 @@ def test_fwd_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
     o, lse = run_fwd(q, k, v, scale, mask, window, rope)
     ro, rl = oracle.attention(q, k, v, scale, mask, window, rope)
     compare(o, lse, ro, rl, TOL[dt], "fwd")
+
+
+# 16-bit D = 64 forwards run either as 128-row work-groups or, when the grid
+# is small, as 64-row work-groups whose two wave pairs take the two halves of
+# the key range and merge in LDS; RF_ATTN_KEY_HALVES forces one or the other.
+# Every D = 64 16-bit case runs both ways, plus cases aimed at the halves:
+# odd tile counts (the second half one tile short), a single tile (the second
+# half empty, so the merge takes -inf from it), rows that see no key.
+D64_CASES = [c for c in FWD_CASES if c[1] == 64 and c[0] != "f32"] + [
+    ("f16", 64, 1, 2, 2, 64, 96, "none", 0, 0.0),        # 3 tiles of 32 keys
+    ("bf16", 64, 1, 2, 2, 40, 20, "none", 0, 0.0),       # one tile
+    ("f16", 64, 1, 3, 1, 200, 120, "causal", 0, 0.0),    # first 80 rows see no key
+    ("bf16", 64, 2, 4, 2, 333, 900, "sliding", 100, 10000.0),
+    ("f16", 64, 1, 2, 2, 70, 4100, "none", 0, 10000.0),  # 129 tiles: re-anchor inside each half
+]
+
+
+@pytest.mark.parametrize("halves", ["0", "1"])
+@pytest.mark.parametrize("dt,D,B,Hq,Hkv,Nq,Nk,mask,window,rope", D64_CASES)
+def test_fwd_d64_both_layouts(monkeypatch, halves, dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
+    monkeypatch.setenv("RF_ATTN_KEY_HALVES", halves)
+    seed = zlib.crc32(repr((dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope)).encode()) % 10_000
+    q, k, v = gen_qkv(B, Hq, Hkv, Nq, Nk, D, dt, seed)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case fwd halves={halves} {dt} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} {mask} W={window} rope={rope}", flush=True)
+    o, lse = run_fwd(q, k, v, scale, mask, window, rope)
+    ro, rl = oracle.attention(q, k, v, scale, mask, window, rope)
+    compare(o, lse, ro, rl, TOL[dt], f"fwd halves={halves}")
+
+
+@pytest.mark.parametrize("halves", ["0", "1"])
+def test_fwd_d64_alibi_both_layouts(monkeypatch, halves):
+    from workloads import alibi_slopes
+    monkeypatch.setenv("RF_ATTN_KEY_HALVES", halves)
+    q, k, v = gen_qkv(1, 4, 2, 150, 400, 64, "f16", 77)
+    sl = alibi_slopes(4)
+    print(f"case alibi fwd halves={halves}", flush=True)
+    for mask, rope in (("causal", 0.0), ("none", 10000.0)):
+        dev = torch.device("cuda")
+        o, lse = rf.fwd(q.to(dev), k.to(dev), v.to(dev), scale=0.125, mask=mask, rope_base=rope, alibi_slopes=sl)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention(q, k, v, 0.125, mask, 0, rope, alibi_slopes=sl)
+        compare(o, lse, ro, rl, TOL["f16"], f"alibi halves={halves} {mask}")
 
 
 @pytest.mark.parametrize("scale", [0.125, 0.69, 0.7, 1.0, 4.0])
