@@ -410,9 +410,10 @@ rf_status rf_softmax_topk(const void* x, float* values, int* indices, int rows, 
     const int rpb = (rf::TOPK_THREADS / 64) * (64 / lpr);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     const int vpl = (E + lpr - 1) / lpr;
+    const int vec = dtype != RF_F32 && E % 8 == 0 && ((uintptr_t)x & 15u) == 0;
 #define RF_TK(KERNEL, TYPE, N, L)                                                                          \
     hipLaunchKernelGGL((rf::KERNEL<TYPE, N, L>), grid, dim3(rf::TOPK_THREADS), 0, stream, (const TYPE*)x, values, \
-                       indices, rows, E, k)
+                       indices, rows, E, k, vec)
 #define RF_TK_V(KERNEL, TYPE, L)                   \
     if (vpl <= 1) RF_TK(KERNEL, TYPE, 1, L);       \
     else if (vpl <= 2) RF_TK(KERNEL, TYPE, 2, L);  \

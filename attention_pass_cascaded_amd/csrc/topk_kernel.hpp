@@ -7,8 +7,9 @@
 //   level 3 (TopK)  the k largest p_e = 2^((x_e - m) log2 e) / l with indices
 //                                                                  (reads m, l)
 // A group of LPR lanes per row (16 when E <= 256 and k <= 16, else 64), the
-// row held in registers (lane l of the group owns elements l, l + LPR, ...):
-// the row is read from HBM once and every level runs on it in place.  The k
+// row held in registers (float32: lane l of the group owns elements l,
+// l + LPR, ...; 16-bit: VPL consecutive elements per lane): the row is read
+// from HBM once and every level runs on it in place.  The k
 // largest p are the k largest x (exp is increasing), so the selection
 // compares the exact input values; ties go to the lower index, which makes
 // the result unique.  Each of the k rounds takes the group's best untaken
@@ -34,7 +35,7 @@ __device__ __forceinline__ bool topk_better(float v, int i, float w, int j) {
 template <typename T, int VPL, int LPR>
 __global__ __launch_bounds__(TOPK_THREADS) void softmax_topk_kernel(const T* __restrict__ x, float* __restrict__ values,
                                                                     int* __restrict__ indices, int rows, int E,
-                                                                    int k) {
+                                                                    int k, int /*vec*/) {
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int RPW = 64 / LPR;  // rows per wavefront
     const int lane = threadIdx.x & 63;
@@ -158,10 +159,12 @@ __device__ __forceinline__ float topk_group_sum(float v) {
     return v;
 }
 
+// vec: E is a multiple of 8 and x is 16-byte aligned, so with VPL a
+// multiple of 8 each lane reads its elements as whole 16-byte chunks.
 template <typename T, int VPL, int LPR>
 __global__ __launch_bounds__(TOPK_THREADS) void softmax_topk16_kernel(const T* __restrict__ x, float* __restrict__ values,
                                                                       int* __restrict__ indices, int rows, int E,
-                                                                      int k) {
+                                                                      int k, int vec) {
     static_assert(sizeof(T) == 2, "16-bit inputs");
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int RPW = 64 / LPR;
@@ -171,15 +174,32 @@ __global__ __launch_bounds__(TOPK_THREADS) void softmax_topk16_kernel(const T* _
     const bool row_ok = row < rows;
     const unsigned short* xr = (const unsigned short*)x + (row_ok ? row : 0) * (long long)E;
 
-    // lane `sub` of the group owns elements sub, sub + LPR, ...; absent ones
-    // get key 0 (below every present key) and x = -inf
+    // lane `sub` of the group owns the VPL consecutive elements from
+    // sub * VPL (the selection below does not depend on which lane holds an
+    // element: keys carry the index); absent ones get key 0 (below every
+    // present key) and x = -inf
+    const int e0 = sub * VPL;
+    unsigned short raw[VPL];
+    if (VPL % 8 == 0 && vec) {
+#pragma unroll
+        for (int c = 0; c < VPL / 8; ++c) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (e0 + 8 * c < E) u = *(const uint4*)(xr + e0 + 8 * c);  // E % 8 == 0: whole chunk in the row
+            const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int h = 0; h < 8; ++h) raw[8 * c + h] = (unsigned short)(w[h / 2] >> (16 * (h % 2)));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) raw[i] = xr[min(e0 + i, E - 1)];  // in-row address for every lane
+    }
     unsigned key[VPL];
     float xv[VPL];
     unsigned best = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        const int e = sub + LPR * i;
-        const unsigned b = xr[min(e, E - 1)];  // in-row address for every lane: no branch
+        const int e = e0 + i;
+        const unsigned b = raw[i];
         xv[i] = e < E ? to_f32(__builtin_bit_cast(T, (unsigned short)b)) : -INFINITY;
         key[i] = e < E ? (topk_mono16(b) << 16) | (0xFFFFu - (unsigned)e) : 0u;
         best = max(best, key[i]);

@@ -56,6 +56,20 @@ def test_softmax_topk_matches_oracle(dt, rows, E, k):
     check(x, k, vals, idx)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_softmax_topk_unaligned_rows(dt):
+    """Rows that start 2 bytes past a 16-byte boundary (E a multiple of 8):
+    the element loads fall back from 16-byte chunks to single elements."""
+    rows, E, k = 21, 256, 8
+    flat = gen_logits(1, rows * E + 1, dt, seed=4242).reshape(-1)
+    print(f"case topk unaligned {dt}", flush=True)
+    xg = flat.cuda()[1:].view(rows, E)
+    assert xg.data_ptr() % 16 == 2
+    vals, idx = rf.softmax_topk(xg, k)
+    torch.cuda.synchronize()
+    check(flat[1:].view(rows, E), k, vals, idx)
+
+
 def test_softmax_topk_all_ties():
     x = torch.zeros((4, 96), dtype=torch.bfloat16)
     vals, idx = rf.softmax_topk(x.cuda(), 10)
