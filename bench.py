@@ -46,7 +46,13 @@ KERNEL_SOURCES = {
     "fwd": ["attention_pass_cascaded_amd/csrc/fwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "decode": ["attention_pass_cascaded_amd/csrc/decode_mfma_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "layernorm": ["attention_pass_cascaded_amd/csrc/layernorm_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "bwd": ["attention_pass_cascaded_amd/csrc/bwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/fwd_kernel.hpp",
+            "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "topk": ["attention_pass_cascaded_amd/csrc/topk_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "merge": ["attention_pass_cascaded_amd/csrc/merge_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "rope": ["attention_pass_cascaded_amd/csrc/rope_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
 }
+GRAPH_TIMING = True  # bench.py --no-graph turns the captured-graph timings off (counter passes)
 
 
 def kernel_hash(kind: str) -> str:
@@ -134,6 +140,8 @@ def time_graph(fn, calls: int = 20, replays: int = 50) -> float:
     without the host's per-call cost (Python, ctypes, launch), the way a
     serving loop issues decode steps.  The calls must not allocate."""
     import torch
+    if not GRAPH_TIMING:
+        return float("nan")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -256,8 +264,8 @@ def run_topk(steps, warmup):
     # cost, so the roofline uses the time inside a captured graph
     ms_graph = time_graph(call)
     byts = x.numel() * x.element_size() + 8 * w["rows"] * w["k"]
-    gbs = byts / (ms_graph * 1e-3) / 1e9
-    return {"workload": w["name"], "ms": ms, "ms_graph": ms_graph, "GB/s": gbs,
+    gbs = byts / ((ms if ms_graph != ms_graph else ms_graph) * 1e-3) / 1e9  # eager time without the graph
+    return {"workload": w["name"], "ms": ms, "ms_graph": ms_graph if ms_graph == ms_graph else None, "GB/s": gbs,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "traffic": None},
             "alg_mb": byts / 1e6}
@@ -299,8 +307,8 @@ def run_decode(w, steps, warmup, num_splits=None, keep=False):
     traffic = traffic_from_profiles("decode", w.name)
     res = {
         "workload": w.name, "num_splits": S, "value": gbs, "unit": "GB/s", "ms_per_step": ms,
-        "ms_median": t["median"], "ms_min": t["min"], "ms_step_graph": ms_graph,
-        "GB/s_step_graph": byts / (ms_graph * 1e-3) / 1e9,
+        "ms_median": t["median"], "ms_min": t["min"], "ms_step_graph": ms_graph if ms_graph == ms_graph else None,
+        "GB/s_step_graph": byts / (ms_graph * 1e-3) / 1e9 if ms_graph == ms_graph else None,
         "ms_partial_kernel": ms_part, "ms_merge_kernel": ms_merge,
         "roofline": {"bound": "hbm", "achieved": gbs_part, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs_part / PEAK_HBM_GBS, "traffic": traffic},
@@ -540,9 +548,13 @@ def main():
                     help="decode geometries with every chunk count 8..256 (prints one JSON line)")
     ap.add_argument("--variants", action="store_true", help="the variant table only (prints one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the captured-graph timings of the short launches (for counter passes)")
     ap.add_argument("--rotation-sweep", action="store_true",
                     help="fused RoPE vs rotate-first over N (prints one JSON line per N)")
     args = ap.parse_args()
+    global GRAPH_TIMING
+    GRAPH_TIMING = not args.no_graph
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported. Prefill shards "
