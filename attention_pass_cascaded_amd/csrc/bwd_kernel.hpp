@@ -45,16 +45,8 @@ struct BwdParams {
 constexpr int BWD_THREADS = 256;
 
 // Waves per SIMD the D = 64 dq and dk/dv kernels are compiled for, and the
-// query tile of the dk/dv kernel at D = 64 (tuning knobs, measured).
-#ifndef RF_BWD_DQ_WAVES
-#define RF_BWD_DQ_WAVES 2
-#endif
-#ifndef RF_BWD_KV_WAVES
-#define RF_BWD_KV_WAVES 2
-#endif
-#ifndef RF_BWD_BQ64
-#define RF_BWD_BQ64 64
-#endif
+// query tile of the dk/dv kernel at D = 64: RF_BWD_DQ_WAVES, RF_BWD_KV_WAVES
+// and RF_BWD_BQ64 in tuned.hpp.
 
 // ---------------------------------------------------------------- D_i
 template <typename T, int D>

@@ -31,6 +31,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "tuned.hpp"
 
 namespace rf {
 
@@ -53,11 +54,8 @@ struct FwdCfg {
 };
 
 // Waves per SIMD the non-RoPE D=64 instance is compiled for (register budget
-// 512 / waves); 4 measured best for the causal fp16 workload (LDS allows 4
-// work-groups per CU).  The other instances need more registers and get 2.
-#ifndef RF_FWD_WAVES_D64
-#define RF_FWD_WAVES_D64 4
-#endif
+// 512 / waves): RF_FWD_WAVES_D64 in tuned.hpp.  The other instances need more
+// registers and get 2.
 
 // Work-group order (one-dimensional grid of B*Hq*S*nqb query blocks of
 // FWD_BM rows); returns the query block qb and bx = (b * Hq + h) * S + split.

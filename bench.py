@@ -43,11 +43,12 @@ PAGES_HEADLINE_MS = 0.488  # AttnFuse, causal fp16 B4 H12 N4096 D64, H100 NVL (T
 # Files whose content defines each kernel: HBM counter figures are used only
 # while these are unchanged since the counters were taken.
 KERNEL_SOURCES = {
-    "fwd": ["attention_pass_cascaded_amd/csrc/fwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
+    "fwd": ["attention_pass_cascaded_amd/csrc/fwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp",
+            "attention_pass_cascaded_amd/csrc/tuned.hpp"],
     "decode": ["attention_pass_cascaded_amd/csrc/decode_mfma_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "layernorm": ["attention_pass_cascaded_amd/csrc/layernorm_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "bwd": ["attention_pass_cascaded_amd/csrc/bwd_kernel.hpp", "attention_pass_cascaded_amd/csrc/fwd_kernel.hpp",
-            "attention_pass_cascaded_amd/csrc/common.hpp"],
+            "attention_pass_cascaded_amd/csrc/common.hpp", "attention_pass_cascaded_amd/csrc/tuned.hpp"],
     "topk": ["attention_pass_cascaded_amd/csrc/topk_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "merge": ["attention_pass_cascaded_amd/csrc/merge_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
     "rope": ["attention_pass_cascaded_amd/csrc/rope_kernel.hpp", "attention_pass_cascaded_amd/csrc/common.hpp"],
