@@ -466,6 +466,27 @@ def sample_clock(fn, seconds: float = 1.5):
     return {"tool": None, "MHz": None, "raw": raw[-600:]}
 
 
+def shape_sweep(steps: int, warmup: int):
+    """The fused forward across shapes: B=4, H=16, N = Nq = Nk from 1024 to
+    16384, D 64 and 128, fp16 and bf16, causal and unmasked; one JSON line per
+    shape (time, TFLOP/s, fraction of the MFMA peak).  The number of timed
+    calls shrinks for the large shapes so every shape takes about 0.2 s."""
+    import dataclasses
+    from workloads import Workload
+    for D in (64, 128):
+        for dt in ("f16", "bf16"):
+            for mask in ("causal", "none"):
+                for N in (1024, 2048, 4096, 8192, 16384):
+                    w = Workload(f"{mask}_{dt}_b4h16_n{N}_d{D}", B=4, Hq=16, Hkv=16, Nq=N, Nk=N, D=D, dtype=dt,
+                                 scale=1.0 / math.sqrt(D), mask=mask, seed=42)
+                    est_ms = alg_flops(w) / (800e12 * 1e-3)  # at ~800 TFLOP/s
+                    n = int(max(10, min(steps, 200.0 / max(est_ms, 1e-3))))
+                    r, _ = run_prefill(dataclasses.replace(w), n, max(3, min(warmup, n // 4)))
+                    print(json.dumps({"shape": w.name, "B": w.B, "H": w.Hq, "N": N, "D": D, "dtype": dt, "mask": mask,
+                                      "ms": r["ms"], "ms_median": r["ms_median"], "TFLOP/s": r["TFLOP/s"],
+                                      "mfma_frac": r["roofline"]["frac"], "steps": n}), flush=True)
+
+
 def rotation_sweep(steps: int, warmup: int, Ns=(512, 1024, 2048, 4096, 8192, 16384)):
     """Fused RoPE vs rotate-first, causal fp16 B=4 H=12 D=64 (AttnFuse Table 4's comparison).
 
@@ -549,6 +570,8 @@ def main():
                     help="decode geometries with every chunk count 8..256 (prints one JSON line)")
     ap.add_argument("--variants", action="store_true", help="the variant table only (prints one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="the fused forward over N, D, dtype and mask at B=4 H=16 (one JSON line per shape)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the captured-graph timings of the short launches (for counter passes)")
     ap.add_argument("--rotation-sweep", action="store_true",
@@ -574,6 +597,9 @@ def main():
         return
     if args.rotation_sweep:
         rotation_sweep(args.steps, args.warmup)
+        return
+    if args.shape_sweep:
+        shape_sweep(args.steps, args.warmup)
         return
     if args.decode_sweep:
         print(json.dumps({"decode_geometries": decode_geometries(args.steps, args.warmup, sweep=True)}), flush=True)
