@@ -39,11 +39,24 @@ namespace rf {
 // operands keep ~16 mantissa bits; S then takes three MFMAs (hi.hi, hi.lo,
 // lo.hi).  Used for bf16 with RoPE, where rounding the rotated q and k to a
 // single bf16 dominates the output error.
-template <typename T, int D, bool SPLITK = false, bool KH = false>
+// Work-group layouts (template parameter KH):
+//  0: 4 waves, 128 query rows, one key stream;
+//  1: key halves, 4 waves, 64 rows: two groups of 2 waves, 32-key tiles;
+//  2: key halves, 8 waves, 128 rows: two groups of 4 waves, 64-key tiles.
+template <int KH>
+struct FwdLayout {
+    static constexpr int WAVES = KH == 2 ? 8 : FWD_WAVES;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int GROUPS = KH ? 2 : 1;       // key streams
+    static constexpr int GWAVES = WAVES / GROUPS;   // waves (32-row slots) per stream
+    static constexpr int BM = 32 * GWAVES;          // query rows per work-group
+};
+
+template <typename T, int D, bool SPLITK = false, int KH = 0>
 struct FwdCfg {
     static constexpr bool F32 = sizeof(T) == 4;
-    static constexpr int BN = (F32 || KH) ? 32 : 64;    // keys per tile
-    static constexpr int GT = KH ? FWD_THREADS / 2 : FWD_THREADS;  // threads staging one tile stream
+    static constexpr int BN = (F32 || KH == 1) ? 32 : 64;  // keys per tile
+    static constexpr int GT = 64 * FwdLayout<KH>::GWAVES;  // threads staging one tile stream
     static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
     static constexpr int CPR = D / EPC;                 // chunks per row
     static constexpr int KSTRIDE = D + EPC;             // row pitch (elements), +16 B
@@ -94,20 +107,23 @@ __device__ __forceinline__ void fwd_work_item(const AttnParams& p, int nqb, int&
     }
 }
 
-// KH (key halves, 16-bit D = 64): 64 query rows per work-group, and the
-// work-group's key range is cut in two: waves 0-1 (group 0) take the first
-// half, waves 2-3 (group 1) the second, each with its own 32-key tile stream
-// and LDS double buffer; at the end group 1 hands (O, m, l) to group 0
-// through LDS and group 0 merges them (the LSE merge of two partial states,
-// RedFuser Fig. 13).  The longest chain of tile steps a work-group runs is
-// halved, which is what bounds a causal launch whose grid fits the GPU in
-// one wave of work-groups.
-template <typename T, int D, bool ROPE, bool ALIBI, bool KH = false>
-__global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2) void attn_fwd_kernel(AttnParams p) {
+// KH (key halves, 16-bit D = 64): the work-group's key range is cut in two:
+// the first group of waves takes the first half, the second group the second,
+// each with its own tile stream and LDS double buffer; at the end group 1
+// hands (O, m, l) to group 0 through LDS and group 0 merges them (the LSE
+// merge of two partial states, RedFuser Fig. 13).  The longest chain of tile
+// steps a work-group runs is halved, which is what bounds a causal launch
+// whose grid fits the GPU in about one wave of work-groups.  KH = 1 keeps 4
+// waves (64 rows, 32-key tiles); KH = 2 has 8 waves (128 rows, 64-key tiles,
+// each group staging its tiles exactly as the 4-wave 128-row kernel does).
+template <typename T, int D, bool ROPE, bool ALIBI, int KH = 0>
+__global__ __launch_bounds__(FwdLayout<KH>::THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_WAVES_D64 : 2)
+void attn_fwd_kernel(AttnParams p) {
     constexpr bool SPLITK = ROPE && sizeof(T) == 2 && !__is_same(T, _Float16);
+    using L = FwdLayout<KH>;
     using C = FwdCfg<T, D, SPLITK, KH>;
     constexpr int GT = C::GT;
-    constexpr int BM = KH ? FWD_BM / 2 : FWD_BM;  // query rows per work-group
+    constexpr int BM = L::BM;  // query rows per work-group
     constexpr bool F32 = C::F32;
     constexpr int BN = C::BN;
     constexpr int EPC = C::EPC;
@@ -136,9 +152,9 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
     const int l32 = lane & 31;
     const int hi = lane >> 5;
     // KH: group (key half) of this wave, its row slot, and the thread's index in the group
-    const int grp = KH ? wave >> 1 : 0;
-    const int rw = KH ? wave & 1 : wave;
-    const int gtid = KH ? tid & (GT - 1) : tid;
+    const int grp = KH ? wave / L::GWAVES : 0;
+    const int rw = KH ? wave % L::GWAVES : wave;
+    const int gtid = KH ? tid % GT : tid;
     T* const gsm = KH ? smem + grp * 2 * C::STAGE : smem;  // this group's two stages
 
     const int nqb = (p.Nq + BM - 1) / BM;
@@ -601,28 +617,29 @@ __global__ __launch_bounds__(FWD_THREADS, (D == 64 && !ROPE && !ALIBI) ? RF_FWD_
         // group 1 hands its state to group 0 through LDS, element-major
         // ([value][row slot][lane]) so the 64 lanes hit 64 banks
         constexpr int NV = NDB * 16 + 2;
+        constexpr int RS = L::GWAVES;  // row slots
         float* xs = (float*)smem;
-        static_assert(2 * NV * 64 * sizeof(float) <= sizeof(smem), "merge area");
+        static_assert(RS * NV * 64 * sizeof(float) <= sizeof(smem), "merge area");
         __syncthreads();  // every wave is done with the tile buffers
         if (grp == 1) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) xs[((db * 16 + j) * 2 + rw) * 64 + lane] = oacc[db][j];
-            xs[((NV - 2) * 2 + rw) * 64 + lane] = m_ref;
-            xs[((NV - 1) * 2 + rw) * 64 + lane] = l_run;
+                for (int j = 0; j < 16; ++j) xs[((db * 16 + j) * RS + rw) * 64 + lane] = oacc[db][j];
+            xs[((NV - 2) * RS + rw) * 64 + lane] = m_ref;
+            xs[((NV - 1) * RS + rw) * 64 + lane] = l_run;
         }
         __syncthreads();
         if (grp == 1) return;
-        const float m1 = xs[((NV - 2) * 2 + rw) * 64 + lane];
-        const float l1 = xs[((NV - 1) * 2 + rw) * 64 + lane];
+        const float m1 = xs[((NV - 2) * RS + rw) * 64 + lane];
+        const float l1 = xs[((NV - 1) * RS + rw) * 64 + lane];
         const float mm = fmaxf(m_ref, m1);
         const float a0 = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mm);  // -inf - -inf would be NaN
         const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[db][j] = a0 * oacc[db][j] + a1 * xs[((db * 16 + j) * 2 + rw) * 64 + lane];
+            for (int j = 0; j < 16; ++j) oacc[db][j] = a0 * oacc[db][j] + a1 * xs[((db * 16 + j) * RS + rw) * 64 + lane];
         l_run = a0 * l_run + a1 * l1;
         m_ref = mm;
     }

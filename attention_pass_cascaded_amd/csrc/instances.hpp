@@ -14,12 +14,13 @@ namespace rf {
 
 // work-groups of an instance that fit on one CU (cached per instance; the
 // same for every gfx950 device); 0 if the query fails
-template <typename T, int D, bool ROPE, bool ALIBI, bool KH>
+template <typename T, int D, bool ROPE, bool ALIBI, int KH>
 int fwd_resident() {
     static std::atomic<int> resident{0};
     int r = resident.load(std::memory_order_relaxed);
     if (r == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, attn_fwd_kernel<T, D, ROPE, ALIBI, KH>, FWD_THREADS, 0) != hipSuccess) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, attn_fwd_kernel<T, D, ROPE, ALIBI, KH>,
+                                                         FwdLayout<KH>::THREADS, 0) != hipSuccess) {
             r = 0;
             (void)hipGetLastError();  // a failed query only turns the snake order off
         }
@@ -29,39 +30,54 @@ int fwd_resident() {
     return r;
 }
 
-template <typename T, int D, bool ROPE, bool ALIBI, bool KH>
+template <typename T, int D, bool ROPE, bool ALIBI, int KH>
 hipError_t fwd_launch_one(const AttnParams& p, hipStream_t s) {
-    constexpr int BM = KH ? FWD_BM / 2 : FWD_BM;
+    constexpr int BM = FwdLayout<KH>::BM;
     AttnParams q = p;
     q.launch_runs = fwd_resident<T, D, ROPE, ALIBI, KH>();
     dim3 grid((unsigned)(p.B * p.Hq * p.num_splits * ((p.Nq + BM - 1) / BM)));
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI, KH>), grid, dim3(FWD_THREADS), 0, s, q);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, ROPE, ALIBI, KH>), grid, dim3(FwdLayout<KH>::THREADS), 0, s, q);
     return hipGetLastError();
 }
 
-// Key halves (16-bit D = 64, not split mode) when twice the 128-row grid
-// still fits in the work-groups the GPU holds at once: then every work-group
-// starts at launch and halving the longest chain of tile steps shortens the
-// launch.  Measured slower once the doubled grid needs a second round (the
-// 32-key steps of the halves cost more per key).  The environment variable
-// RF_ATTN_KEY_HALVES=0 or =1 overrides the choice (read at every call).
+// Work-group layout of the 16-bit D = 64 forward (not split mode), from
+// same-box timings of the three layouts over grid sizes (g = 128-row query
+// blocks, P = CU count, R_k = work-groups of layout k one CU holds):
+//  * unmasked and P <= g <= P * R_2 (every 8-wave group resident at launch):
+//    layout 2, the 8-wave key halves (B1 H8 N8192: 171 vs 181 us for layout
+//    0 and 198 for layout 1; B2 H16 N2048: 47.6 / 49.1 / 53.8; with RoPE, one
+//    group per CU, B1 H8 N4096: 63 / 78 / 82);
+//  * otherwise layout 1, the 64-row key halves, when 2g <= P * R_1 (causal
+//    and windowed masks; unmasked RoPE or ALiBi grids only below one block
+//    per CU): it halves the longest chain of tile steps (B1 H8 N4096 causal
+//    46 vs 60 us), but its 32-key steps cost more per key once the grid fills
+//    the GPU;
+//  * else layout 0.
+// The environment variable RF_ATTN_KEY_HALVES=0, 1 or 2 forces a layout (read
+// at every call).
 template <typename T, int D, bool ROPE, bool ALIBI>
 hipError_t fwd_launch_pick(const AttnParams& p, hipStream_t s) {
     if constexpr (D == 64 && sizeof(T) == 2) {
         if (!p.split_mode) {
             const char* env = std::getenv("RF_ATTN_KEY_HALVES");
-            bool kh;
-            if (env && (env[0] == '0' || env[0] == '1') && env[1] == 0) {
-                kh = env[0] == '1';
+            int kh = 0;
+            if (env && env[0] >= '0' && env[0] <= '2' && env[1] == 0) {
+                kh = env[0] - '0';
             } else {
                 const long long g = (long long)p.B * p.Hq * p.num_splits * ((p.Nq + FWD_BM - 1) / FWD_BM);
-                const long long slots = (long long)p.cu_count * fwd_resident<T, D, ROPE, ALIBI, true>();
-                kh = g > 0 && 2 * g <= slots;
+                const long long P = p.cu_count;
+                const bool uniform = p.mask == RF_MASK_NONE;
+                if (uniform && g >= P && g <= P * fwd_resident<T, D, ROPE, ALIBI, 2>())
+                    kh = 2;
+                else if (g > 0 && 2 * g <= P * fwd_resident<T, D, ROPE, ALIBI, 1>() &&
+                         (!uniform || (!ROPE && !ALIBI) || g < P))
+                    kh = 1;
             }
-            if (kh) return fwd_launch_one<T, D, ROPE, ALIBI, true>(p, s);
+            if (kh == 1) return fwd_launch_one<T, D, ROPE, ALIBI, 1>(p, s);
+            if (kh == 2) return fwd_launch_one<T, D, ROPE, ALIBI, 2>(p, s);
         }
     }
-    return fwd_launch_one<T, D, ROPE, ALIBI, false>(p, s);
+    return fwd_launch_one<T, D, ROPE, ALIBI, 0>(p, s);
 }
 
 template <typename T, int D>

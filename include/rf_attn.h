@@ -80,11 +80,13 @@ typedef enum { RF_MASK_NONE = 0, RF_MASK_CAUSAL = 1, RF_MASK_SLIDING = 2 } rf_ma
  * lse = -inf), Hq, Hkv >= 1, D in {64, 128}.  scale >= 0 multiplies q'.k'.
  * mask_kind: rf_mask.  window: W for RF_MASK_SLIDING, ignored otherwise.
  * rope_base: > 0 enables RoPE with that base.
- * 16-bit D = 64 launches whose grid is small (twice the 128-row grid fits in
- * the work-groups the GPU holds at once) run each work-group's key range as
- * two halves merged on chip; the environment variable RF_ATTN_KEY_HALVES=0
- * or =1 forces the choice (read at every call).  Both layouts compute the
- * same quantity; the summation order differs.
+ * 16-bit D = 64 launches whose grid is small (at most about two 128-row
+ * query blocks per compute unit) run each work-group's key range as two
+ * halves merged on chip, either in 64-row work-groups of 4 waves (layout 1)
+ * or in 128-row work-groups of 8 waves (layout 2, unmasked grids of one to
+ * two blocks per compute unit); the environment variable RF_ATTN_KEY_HALVES=0, 1 or 2 forces a
+ * layout (read at every call).  All layouts compute the same quantity; the
+ * summation order differs.
  */
 rf_status rf_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int Nq, int Nk, int D,

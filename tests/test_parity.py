@@ -105,10 +105,12 @@ def test_fwd_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
     compare(o, lse, ro, rl, TOL[dt], "fwd")
 
 
-# 16-bit D = 64 forwards run either as 128-row work-groups or, when the grid
-# is small, as 64-row work-groups whose two wave pairs take the two halves of
-# the key range and merge in LDS; RF_ATTN_KEY_HALVES forces one or the other.
-# Every D = 64 16-bit case runs both ways, plus cases aimed at the halves:
+# 16-bit D = 64 forwards run as 128-row work-groups of 4 waves (layout 0) or,
+# when the grid is small, with the key range cut in two halves that two groups
+# of waves run and merge in LDS: 64-row work-groups of two wave pairs
+# (layout 1) or 128-row work-groups of two 4-wave groups (layout 2);
+# RF_ATTN_KEY_HALVES forces a layout.
+# Every D = 64 16-bit case runs all three ways, plus cases aimed at the halves:
 # odd tile counts (the second half one tile short), a single tile (the second
 # half empty, so the merge takes -inf from it), rows that see no key.
 D64_CASES = [c for c in FWD_CASES if c[1] == 64 and c[0] != "f32"] + [
@@ -120,7 +122,7 @@ D64_CASES = [c for c in FWD_CASES if c[1] == 64 and c[0] != "f32"] + [
 ]
 
 
-@pytest.mark.parametrize("halves", ["0", "1"])
+@pytest.mark.parametrize("halves", ["0", "1", "2"])
 @pytest.mark.parametrize("dt,D,B,Hq,Hkv,Nq,Nk,mask,window,rope", D64_CASES)
 def test_fwd_d64_both_layouts(monkeypatch, halves, dt, D, B, Hq, Hkv, Nq, Nk, mask, window, rope):
     monkeypatch.setenv("RF_ATTN_KEY_HALVES", halves)
@@ -133,7 +135,7 @@ def test_fwd_d64_both_layouts(monkeypatch, halves, dt, D, B, Hq, Hkv, Nq, Nk, ma
     compare(o, lse, ro, rl, TOL[dt], f"fwd halves={halves}")
 
 
-@pytest.mark.parametrize("halves", ["0", "1"])
+@pytest.mark.parametrize("halves", ["0", "1", "2"])
 def test_fwd_d64_alibi_both_layouts(monkeypatch, halves):
     from workloads import alibi_slopes
     monkeypatch.setenv("RF_ATTN_KEY_HALVES", halves)
