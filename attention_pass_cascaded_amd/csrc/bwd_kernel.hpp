@@ -514,10 +514,14 @@ __global__ __launch_bounds__(BWD_THREADS, D == 64 ? RF_BWD_KV_WAVES : 1) void at
             const int u = i * BWD_THREADS + tid;
             dreg[i] = buf_load16(drs, ((unsigned)(q0 + u / CPR) * D + (u % CPR) * EPC) * (unsigned)sizeof(T));
         }
-        const int r = tid % BQ;
-        const bool in = q0 + r < p.Nq;
-        if (tid < BQ) sreg = in ? lse_log2(p.lse[base + q0 + r]) : INFINITY;
-        else if (tid < 2 * BQ) sreg = in ? p.drow[base + q0 + r] : 0.f;
+        // lse ([0, BQ)) and row terms ([BQ, 2 BQ)) as loaded; the lse's log2
+        // form and the values of rows past Nq are set at the LDS store, so no
+        // instruction here waits on these loads (or, through the in-order
+        // load counter, on the tile loads above)
+        if (tid < 2 * BQ) {
+            const float* src = tid < BQ ? p.lse : p.drow;
+            sreg = src[base + min(q0 + tid % BQ, p.Nq - 1)];
+        }
     };
     auto store_tile = [&](int stage, int it) {
         int hh, q0;
@@ -557,7 +561,10 @@ __global__ __launch_bounds__(BWD_THREADS, D == 64 ? RF_BWD_KV_WAVES : 1) void at
             const int u = i * BWD_THREADS + tid;
             *(uint4*)(ds_ + (u / CPR) * KS + (u % CPR) * EPC) = dreg[i];
         }
-        if (tid < 2 * BQ) fs_[tid] = sreg;  // [0, BQ): lse2, [BQ, 2 BQ): drow
+        if (tid < 2 * BQ) {  // [0, BQ): lse in log2 units, [BQ, 2 BQ): drow
+            const bool in = q0 + tid % BQ < p.Nq;
+            fs_[tid] = tid < BQ ? (in ? lse_log2(sreg) : INFINITY) : (in ? sreg : 0.f);
+        }
     };
 
     const int tr_row = 4 * hi + ((lane & 15) >> 2);

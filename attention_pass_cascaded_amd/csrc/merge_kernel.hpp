@@ -2,11 +2,11 @@
 // and level-2 sum of the cascade applied over chunks, RedFuser Fig. 4):
 //   M = max_c lse_c,  lse = M + ln sum_c exp(lse_c - M),
 //   O = sum_c exp(lse_c - lse) O_c,  rounded once to the output dtype.
-// One work-group per row.  Each wavefront first reduces the row's chunk lse
-// values (max, then the sum of 2^(lse_c - max)) across its lanes; then the threads
-// split the chunks into NSL slices, each thread streaming 4 consecutive d of
-// its chunks with 16-byte loads (all in flight at once), and the slices are
-// summed through LDS.
+// One work-group per row.  Each wavefront reduces the row's chunk lse values
+// (max, then the sum of 2^(lse_c - max)) across its lanes; the threads split
+// the chunks into NSL slices, each thread taking 4 consecutive d of its chunks
+// with 16-byte loads (its first chunks issued together with the reduction's
+// loads), and the slices are summed through LDS.
 #pragma once
 
 #include "common.hpp"
@@ -57,26 +57,58 @@ __global__ __launch_bounds__(MRG_THREADS) void lse_merge_kernel(const float* __r
     const int d4 = tid % TPS;
     const float* lp = lse_part + row * S;
 
+    // The first PB chunks of this thread's slice (O partial and chunk lse) are
+    // loaded before the row's lse reduction, so their latency overlaps the
+    // reduction's own loads: a row with at most PB * NSL chunks is merged
+    // after one round trip to memory.
+    // (Buffer loads: a chunk past S reads zeros without a branch, so no wait
+    // separates these loads; its weight is zeroed below.)
+    constexpr int PB = 8;
+    const int lane = tid & 63;
+    float4 xo[PB];
+    float xl[PB], l0;
+    const float4* op = (const float4*)(o_part + row * (size_t)S * D) + d4;
+    {
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(o_part + row * (size_t)S * D, S * D * (int)sizeof(float));
+        const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lp, S * (int)sizeof(float));
+#pragma unroll
+        for (int k = 0; k < PB; ++k) {
+            const unsigned c = (unsigned)(slice + NSL * k);
+            xo[k] = __builtin_bit_cast(float4, buf_load16(ors, (c * D + 4u * d4) * (unsigned)sizeof(float)));
+            xl[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (int)(c * sizeof(float)), 0, 0));
+        }
+        l0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (int)(lane * sizeof(float)), 0, 0));
+    }
+
     // level 1 and level 2 over the chunks (log2 units): every wavefront takes
     // the row's chunk lse values one per lane (chunks c, c + 64, ...) and
     // reduces them with lane butterflies, so all lanes hold the same bits
-    const int lane = tid & 63;
-    float m = -INFINITY;
-    for (int c = lane; c < S; c += 64) m = fmaxf(m, lp[c] * LOG2E);
+    float m = lane < S ? l0 * LOG2E : -INFINITY;
+    for (int c = lane + 64; c < S; c += 64) m = fmaxf(m, lp[c] * LOG2E);
     m = merge_wave_max(m);
     const bool live = m != -INFINITY;
     float tot = 0.f;
-    if (live)
-        for (int c = lane; c < S; c += 64) tot += fast_exp2(fmaf(lp[c], LOG2E, -m));
+    if (live) {
+        tot = lane < S ? fast_exp2(fmaf(l0, LOG2E, -m)) : 0.f;
+        for (int c = lane + 64; c < S; c += 64) tot += fast_exp2(fmaf(lp[c], LOG2E, -m));
+    }
     tot = merge_wave_sum(tot);
     const float lse2 = live ? m + fast_log2(tot) : 0.f;
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {
-        const float4* op = (const float4*)(o_part + row * (size_t)S * D) + d4;
+#pragma unroll
+        for (int k = 0; k < PB; ++k) {
+            // empty chunk: 2^-inf = 0; a chunk past S (read as zeros) gets weight 0
+            const float w = slice + NSL * k < S ? fast_exp2(fmaf(xl[k], LOG2E, -lse2)) : 0.f;
+            acc.x = fmaf(w, xo[k].x, acc.x);
+            acc.y = fmaf(w, xo[k].y, acc.y);
+            acc.z = fmaf(w, xo[k].z, acc.z);
+            acc.w = fmaf(w, xo[k].w, acc.w);
+        }
 #pragma unroll 8
-        for (int c = slice; c < S; c += NSL) {
-            const float w = fast_exp2(fmaf(lp[c], LOG2E, -lse2));  // empty chunk: 2^-inf = 0
+        for (int c = slice + NSL * PB; c < S; c += NSL) {
+            const float w = fast_exp2(fmaf(lp[c], LOG2E, -lse2));
             const float4 x = op[(size_t)c * TPS];
             acc.x = fmaf(w, x.x, acc.x);
             acc.y = fmaf(w, x.y, acc.y);
