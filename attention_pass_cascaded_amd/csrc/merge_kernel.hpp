@@ -59,8 +59,8 @@ __global__ __launch_bounds__(MRG_THREADS) void lse_merge_kernel(const float* __r
 
     // The first PB chunks of this thread's slice (O partial and chunk lse) are
     // loaded before the row's lse reduction, so their latency overlaps the
-    // reduction's own loads: a row with at most PB * NSL chunks is merged
-    // after one round trip to memory.
+    // reduction's own loads: a row of at most 64 chunks (PB * NSL >= 64) is
+    // merged after one round trip to memory.
     // (Buffer loads: a chunk past S reads zeros without a branch, so no wait
     // separates these loads; its weight is zeroed below.)
     constexpr int PB = 8;
