@@ -337,11 +337,14 @@ def test_splitkv_alibi_matches_oracle(dt, D, B, Hq, Hkv, Nq, Nk, S, mask, window
 
 
 # ---------------------------------------------------------------- standalone RoPE (Rotation Calculus)
-@pytest.mark.parametrize("dt,D,N,pos", [("f16", 64, 77, 0), ("bf16", 128, 130, 1000), ("f32", 64, 33, 5),
-                                         ("f16", 128, 1, 32767), ("f32", 128, 300, 1 << 20)])
-def test_rope_rotate_matches_oracle(dt, D, N, pos):
+# several (B, H) layouts of the rows (the kernel indexes rows * N positions)
+@pytest.mark.parametrize("dt,D,N,pos,BH", [("f16", 64, 77, 0, (2, 3)), ("bf16", 128, 130, 1000, (2, 3)),
+                                            ("f32", 64, 33, 5, (2, 3)), ("f16", 128, 1, 32767, (2, 3)),
+                                            ("f32", 128, 300, 1 << 20, (2, 3)), ("bf16", 64, 50, 7, (3, 5)),
+                                            ("f16", 128, 65, 0, (4, 4))])
+def test_rope_rotate_matches_oracle(dt, D, N, pos, BH):
     g = torch.Generator().manual_seed(zlib.crc32(repr(("rope", dt, D, N, pos)).encode()))
-    x = torch.randn((2, 3, N, D), generator=g).to(DT[dt])
+    x = torch.randn((*BH, N, D), generator=g).to(DT[dt])
     ref = oracle.rope_rotate(x, np.arange(N) + pos, 10000.0)          # fp64
     y = rf.rope_rotate(x.cuda(), 10000.0, pos_offset=pos)
     xi = x.cuda().clone()
