@@ -75,3 +75,41 @@ def test_fused_forward_causal_at_largest_kv_head(problem):
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q64, k64, v64, scale, mask="causal")
     compare(o, lse, ro, rl, "fused forward, causal")
+
+
+# D = 64: the largest head is twice as long (Nk * 64 * 2 bytes just under
+# 2 GiB).  The 16-bit D = 64 forward also runs as key halves (layouts 1 and 2),
+# whose second group starts half-way through the keys; with one query block
+# and no mask the halves are [0, ~8.4M) and [~8.4M, Nk), and the needles sit
+# in both, so the on-chip merge of the two halves is checked at the largest
+# offsets the boundary accepts.
+NK64 = 16_777_000       # Nk * 64 * 2 bytes = 2,147,456,000 < 2^31
+
+
+def needles64(h, i):
+    return [NK64 - 1 - 29 * h - 5 * i, 8_400_001 + 131 * h + 7 * i, 3_000_000 + 977 * h + 13 * i]
+
+
+@pytest.fixture(scope="module")
+def problem64():
+    print(f"case max-size head: bf16 D=64 Nk={NK64} Hq={HQ} Hkv={HKV} Nq={NQ}", flush=True)
+    q, k, v = gen_qkv(1, HQ, HKV, NQ, NK64, 64, "bf16", seed=12, device="cuda")
+    k.mul_(0.1)
+    for h in range(HQ):
+        for i in range(NQ):
+            for j in needles64(h, i):
+                k[0, 0, j] = (4.0 * q[0, h, i].float()).to(k.dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q.float().cpu().double().numpy(), k.float().cpu().double().numpy(),
+                              v.float().cpu().double().numpy(), 1 / 8)
+    return q, k, v, ro, rl
+
+
+@pytest.mark.parametrize("layout", ["0", "1", "2"])
+def test_fused_forward_d64_layouts_at_largest_kv_head(problem64, monkeypatch, layout):
+    q, k, v, ro, rl = problem64
+    monkeypatch.setenv("RF_ATTN_KEY_HALVES", layout)
+    print(f"case max-size D=64 forward, layout {layout}", flush=True)
+    o, lse = rf.fwd(q, k, v, scale=1 / 8)
+    torch.cuda.synchronize()
+    compare(o, lse, ro, rl, f"fused forward D=64, layout {layout}")
