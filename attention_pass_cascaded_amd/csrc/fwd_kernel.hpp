@@ -112,8 +112,8 @@ __device__ __forceinline__ void fwd_work_item(const AttnParams& p, int nqb, int&
 // each with its own tile stream and LDS double buffer; at the end group 1
 // hands (O, m, l) to group 0 through LDS and group 0 merges them (the LSE
 // merge of two partial states, RedFuser Fig. 13).  The longest chain of tile
-// steps a work-group runs is halved, which is what bounds a causal launch
-// whose grid fits the GPU in about one wave of work-groups.  KH = 1 keeps 4
+// steps a work-group runs is halved, which shortens a launch whose grid fits
+// the GPU in about one wave of work-groups.  KH = 1 keeps 4
 // waves (64 rows, 32-key tiles); KH = 2 has 8 waves (128 rows, 64-key tiles,
 // each group staging its tiles exactly as the 4-wave 128-row kernel does).
 template <typename T, int D, bool ROPE, bool ALIBI, int KH = 0>
