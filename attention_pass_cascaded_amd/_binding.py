@@ -150,8 +150,8 @@ def _slopes(alibi_slopes, Hq, device):
 # Rotation Calculus on MI355X: causal fp16 B=4 H=12 D=64 with RoPE, fused vs
 # rotate-first; the fused kernel wins up to this key length (the crossover N*
 # of the measured sweep, `bench.py --rotation-sweep`; repeated sweeps put it
-# between ~2760 and ~2990, where the two modes are within a few percent).
-ROPE_FUSED_MAX_N = 2781
+# between ~2760 and ~3150, where the two modes are within a few percent).
+ROPE_FUSED_MAX_N = 3150
 
 
 def fwd(q, k, v, scale=None, mask="none", window=0, rope_base=0.0, out=None, lse=None,
