@@ -27,6 +27,9 @@ def test_captured_step_matches_eager_on_every_replay():
     qd, kd, vd = gen_qkv(2, 8, 2, 1, 2048, 128, "bf16", seed=23, device=dev)
     x, gam, bet = gen_layernorm(64, 1024, "bf16", seed=24, device=dev)
     logits = gen_logits(128, 256, "bf16", seed=25, device=dev)
+    # an unmasked grid of one 128-row block per CU (8 heads x 32 blocks): the
+    # 8-wave key-halves layout on a 256-CU GPU
+    q2, k2, v2 = gen_qkv(1, 8, 8, 4096, 4096, 64, "f16", seed=26, device=dev)
 
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], device=dev)
@@ -42,7 +45,9 @@ def test_captured_step_matches_eager_on_every_replay():
     rstd = torch.empty(x.shape[:1], device=dev)
     vals = torch.empty((128, 8), device=dev)
     idx = torch.empty((128, 8), dtype=torch.int32, device=dev)
-    outs = (o, lse, dq, dk, dv, od, lsed, y, mean, rstd, vals, idx)
+    o2 = torch.empty_like(q2)
+    lse2 = torch.empty(q2.shape[:3], device=dev)
+    outs = (o, lse, dq, dk, dv, od, lsed, y, mean, rstd, vals, idx, o2, lse2)
 
     def step():
         rf.fwd(q, k, v, scale=0.125, mask="causal", rope_base=10000.0, out=o, lse=lse)
@@ -52,6 +57,7 @@ def test_captured_step_matches_eager_on_every_replay():
         rf.lse_merge(op, lp, out=od, lse=lsed)
         rf.layernorm(x, gam, bet, 1e-5, y=y, mean=mean, rstd=rstd)
         rf.softmax_topk(logits, 8, values=vals, indices=idx)
+        rf.fwd(q2, k2, v2, scale=0.125, out=o2, lse=lse2)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -64,7 +70,7 @@ def test_captured_step_matches_eager_on_every_replay():
     with torch.cuda.graph(graph):
         step()
 
-    inputs = (q, k, v, do, qd, kd, vd, x, logits)
+    inputs = (q, k, v, do, qd, kd, vd, x, logits, q2, k2, v2)
     for rep in range(3):
         gen = torch.Generator(device=dev).manual_seed(100 + rep)
         for t in inputs:
@@ -77,6 +83,8 @@ def test_captured_step_matches_eager_on_every_replay():
             t.zero_()
         step()  # eager, same inputs
         torch.cuda.synchronize()
-        for name, a, b in zip(("o", "lse", "dq", "dk", "dv", "o_dec", "lse_dec", "y", "mean", "rstd", "vals", "idx"),
-                              replayed, outs):
+        names = ("o", "lse", "dq", "dk", "dv", "o_dec", "lse_dec", "y", "mean", "rstd", "vals", "idx",
+                 "o_halves", "lse_halves")
+        assert len(names) == len(outs)
+        for name, a, b in zip(names, replayed, outs):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from eager"
