@@ -135,14 +135,16 @@ rf_status rf_attn_splitkv_fwd_alibi(const void* q, const void* k, const void* v,
  * Table 8).  The pages fix no rule; this one is measured on MI355X.  The
  * partial kernel runs one work-group per (chunk, KV head, batch), so
  *   S = ceil(RF_SPLIT_GROUPS_PER_CU * cu_count / (B * Hkv)),
- * enough work-groups to keep every compute unit streaming, then capped so
- * every chunk keeps at least RF_SPLIT_MIN_KEYS keys (S <= ceil(Nk /
- * RF_SPLIT_MIN_KEYS)), and clamped to [1, 4096].  cu_count <= 0 asks the
- * current device (falls back to 256).  Returns 0 for invalid sizes (B < 1,
- * Hkv < 1, Nk < 0).
+ * about two work-groups per compute unit, then capped so every chunk keeps
+ * at least RF_SPLIT_MIN_KEYS keys (S <= ceil(Nk / RF_SPLIT_MIN_KEYS)), and
+ * clamped to [1, 4096].  (More chunks add merge work that batch-1 steps
+ * feel: with graph-replayed steps this rule is the fastest chunk count, or
+ * within 0.3 %, at batch 1 for AttnFuse Table 8's geometries, and within
+ * 1.2 % at batch 16.)  cu_count <= 0 asks the current device (falls back to
+ * 256).  Returns 0 for invalid sizes (B < 1, Hkv < 1, Nk < 0).
  */
-#define RF_SPLIT_GROUPS_PER_CU 4
-#define RF_SPLIT_MIN_KEYS 256
+#define RF_SPLIT_GROUPS_PER_CU 2
+#define RF_SPLIT_MIN_KEYS 128
 int rf_splitkv_num_splits(int B, int Hkv, int Nk, int cu_count);
 
 /*

@@ -211,11 +211,12 @@ def test_out_buffer_on_another_device_rejected():
 
 
 @pytest.mark.parametrize("B,Hkv,Nk,cu,want", [
-    (16, 8, 32768, 256, 8),      # ceil(4*256 / 128) = 8 chunks of 4096
-    (1, 8, 32768, 256, 128),     # ceil(1024 / 8) = 128, chunks of exactly 256 keys
-    (1, 8, 4096, 256, 16),       # 128 wanted, capped at ceil(4096 / 256) = 16
-    (1, 8, 4097, 256, 17),       # the cap rounds up
-    (16, 8, 16384, 256, 8),
+    (16, 8, 32768, 256, 4),      # ceil(2*256 / 128) = 4 chunks of 8192
+    (1, 8, 32768, 256, 64),      # ceil(512 / 8) = 64 chunks of 512 keys
+    (1, 8, 4096, 256, 32),       # 64 wanted, capped at ceil(4096 / 128) = 32
+    (1, 8, 4097, 256, 33),       # the cap rounds up
+    (16, 8, 16384, 256, 4),
+    (64, 8, 4096, 256, 1),       # 512 (batch, KV head) groups fill the GPU unsplit
     (1, 1, 10, 256, 1),          # fewer keys than one chunk's minimum
     (3, 1, 0, 256, 1),           # no keys: one (empty) chunk
     (1, 1, 1 << 30, 100000, 4096),  # clamped to the ABI's maximum
